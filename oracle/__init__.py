@@ -1,0 +1,9 @@
+"""fp64 CPU oracle (test infrastructure only; never called by the library)."""
+from .pp_oracle import (  # noqa: F401
+    attend,
+    doc_prefix_len,
+    oracle_decode,
+    tail_lists,
+    to_f64,
+    visible_slots,
+)
