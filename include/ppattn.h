@@ -1,0 +1,144 @@
+/*
+ * ppattn.h -- C ABI of the Parallel Prompting decode-step attention library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (Parallel Prompting project page, "How it works", item 1, the
+ * stream mask; arXiv abstract of "Read Once, Answer Many"): P answer streams
+ * of one request are packed after a shared document in one KV cache.  Every
+ * KV slot carries a stream id.  At one decode step each stream has one query
+ * token, and stream s attends only to the document and to its own slots.
+ * The page states that each answer is then the same as decoding its question
+ * alone; this library computes exactly that result, reading the document's
+ * K/V once for all P streams (the page's "one matrix x matrix product"
+ * instead of one vector x matrix product per question).
+ *
+ * Definition of out, for every stream s in [0,P) and head h in [0,H):
+ *   V_s = { j < seq_len : stream_id[j] == 0 || stream_id[j] == s + 1 }
+ *   x_j = scale * dot(q[s,h,:], k_cache[j,h,:])
+ *   out[s,h,:] = sum_{j in V_s} softmax_j(x) * v_cache[j,h,:]
+ *   out[s,h,:] = 0 when V_s is empty.
+ * Id encoding: 0 = document, s+1 = stream s (the page's document id -1 and
+ * streams 0..P-1, shifted by one).  Ids outside {0..P} are visible to no
+ * stream (they are not an error).  No position test is made: every cached
+ * slot precedes the decode query; whether the query's own K/V is already in
+ * the cache is the caller's choice.  The leading run of id-0 slots is the
+ * document fast path; id-0 slots after that run are still visible to every
+ * stream (handled with the streams' own slots).
+ *
+ * Layouts (all row-major, contiguous, caller-owned DEVICE memory, 16-byte
+ * aligned):
+ *   q         [P, H, d]         element type `dtype`
+ *   k_cache   [T >= seq_len, H, d]  element type `dtype`; only the first
+ *   v_cache   [T >= seq_len, H, d]  seq_len slots are ever read
+ *   stream_id [T >= seq_len]    int32
+ *   out       [P, H, d]         element type `dtype` (bf16 results are rounded
+ *                               to nearest even); every element is written
+ * Arithmetic: bf16 or fp32 inputs, fp32 accumulation and softmax.
+ *
+ * Ownership and asynchrony: the library allocates no memory.  Scratch space
+ * is the caller's `workspace` (device memory of at least
+ * pp_attn_workspace_bytes(...) bytes, 16-byte aligned).  Work is enqueued on
+ * `hip_stream` (a hipStream_t; NULL = the null stream) and the call returns
+ * without waiting and without reading device data on the host.  Inputs,
+ * `out` and `workspace` must stay valid until the stream has passed the
+ * call.  Two calls that run at the same time must not share a workspace.
+ * The library keeps no mutable global state besides a once-per-device cache
+ * of device properties; it is safe to call from several host threads.
+ *
+ * Errors: every entry point returns a pp_status_t and never throws or
+ * aborts.  Arguments are checked on the host before any HIP call:
+ *   PP_ERR_INVALID_ARG  null pointer, P/H/seq_len < 1, seq_len or P too
+ *                       large, non-finite scale, misaligned pointer, `out`
+ *                       overlapping an input or the workspace
+ *   PP_ERR_UNSUPPORTED  d not in {64, 128}, unknown dtype
+ *   PP_ERR_WORKSPACE    workspace null or smaller than required
+ *   PP_ERR_HIP          a HIP launch or device query failed
+ * Device data is not validated: NaN/Inf in K/V slots a stream does not see
+ * never reach that stream's output.  pp_last_error_message() gives a
+ * human-readable reason for the calling thread's last failure.
+ */
+#ifndef PPATTN_H
+#define PPATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PP_ABI_VERSION 1
+
+typedef enum {
+  PP_OK = 0,
+  PP_ERR_INVALID_ARG = 1,
+  PP_ERR_UNSUPPORTED = 2,
+  PP_ERR_WORKSPACE = 3,
+  PP_ERR_HIP = 4
+} pp_status_t;
+
+typedef enum { PP_BF16 = 0, PP_F32 = 1 } pp_dtype_t;
+
+/* Largest accepted seq_len and P. */
+#define PP_MAX_SEQ_LEN ((int64_t)1 << 30)
+#define PP_MAX_STREAMS 65535
+#define PP_MAX_HEADS 65535
+
+/* ABI version of the loaded library (PP_ABI_VERSION at build time). */
+int pp_abi_version(void);
+
+/* Static description of a status code. */
+const char* pp_status_string(pp_status_t status);
+
+/* Reason for the calling thread's most recent non-OK status ("" if none). */
+const char* pp_last_error_message(void);
+
+/* Bytes of workspace that pp_attn_decode and pp_attn_decode_batched need for
+ * this shape (the larger of the two).  Returns 0 for arguments that either
+ * entry point would reject. */
+size_t pp_attn_workspace_bytes(int64_t seq_len, int32_t P, int32_t H, int32_t d, pp_dtype_t dtype);
+
+/* One decode step of multi-stream shared-document attention (definition
+ * above).  The document prefix is read once for all streams: its K/V tiles
+ * are staged in LDS and contracted against all P queries of a head with
+ * matrix-core (MFMA) products, split over the document into partial softmax
+ * states; each stream's own slots are gathered by that stream only; partial
+ * states are merged in a fixed order, so results are bitwise reproducible
+ * run to run.  [Parallel Prompting project page, "How it works": stream mask,
+ * document read once per step for all streams.] */
+pp_status_t pp_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* stream_id, int64_t seq_len, int32_t P, int32_t H,
+                           int32_t d, float scale, void* out, pp_dtype_t dtype, void* workspace,
+                           size_t workspace_bytes, void* hip_stream);
+
+/* The same result computed as P independent requests ("batched requests",
+ * one request per question, as a stock serving engine runs them): every
+ * stream reads the whole document's K/V for itself with a per-query
+ * split-K GEMV, then its own slots.  [Parallel Prompting project page,
+ * illustration "Inside decode step" and "How it works": a per-question
+ * request reads the document once per question per step.]  Provided as the
+ * comparison baseline; same arguments and contract as pp_attn_decode. */
+pp_status_t pp_attn_decode_batched(const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* stream_id, int64_t seq_len, int32_t P, int32_t H,
+                                   int32_t d, float scale, void* out, pp_dtype_t dtype,
+                                   void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* The integer visibility plan that both entry points evaluate on the device,
+ * exposed for inspection.  Writes, on `hip_stream`:
+ *   doc_len_out[0]      length of the leading run of id-0 slots (<= seq_len)
+ *   tail_count_out[s]   number of slots j >= doc_len visible to stream s
+ *                       (its own slots and later id-0 slots)
+ *   tail_slots_out[s*tail_capacity + i]  the first min(count, tail_capacity)
+ *                       of those slots, ascending
+ * All three are caller-owned device buffers (int32; tail_slots_out may be
+ * NULL when tail_capacity is 0).  [Project page, "How it works", item 1.]
+ * Errors as above (PP_ERR_INVALID_ARG for null/invalid arguments). */
+pp_status_t pp_attn_plan(const int32_t* stream_id, int64_t seq_len, int32_t P,
+                         int32_t* doc_len_out, int32_t* tail_count_out, int32_t* tail_slots_out,
+                         int64_t tail_capacity, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PPATTN_H */

@@ -1,0 +1,208 @@
+"""Parallel Prompting decode-step attention on AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over the C ABI of ``libppattn.so`` (declared in
+``include/ppattn.h``).  It only marshals arguments: every step of the
+computation runs in the library's HIP kernels.  PyTorch provides device
+memory (output and workspace tensors) and the current HIP stream.
+
+    out = pp_attn_decode(q, k_cache, v_cache, stream_id, seq_len)
+
+q [P, H, d]; k_cache, v_cache [T >= seq_len, H, d] (bf16 or fp32, on the GPU,
+contiguous); stream_id [T] int32 with 0 = document, s+1 = stream s.  See
+the header for the exact definition and contract.
+
+If the library has not been built (``python -m shared_prefix_stream_amd.build``)
+every entry point raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+__all__ = [
+    "PPError",
+    "library_path",
+    "abi_version",
+    "workspace_bytes",
+    "pp_attn_decode",
+    "pp_attn_decode_batched",
+    "pp_attn_plan",
+    "PP_OK",
+    "PP_ERR_INVALID_ARG",
+    "PP_ERR_UNSUPPORTED",
+    "PP_ERR_WORKSPACE",
+    "PP_ERR_HIP",
+    "PP_BF16",
+    "PP_F32",
+]
+
+PP_OK, PP_ERR_INVALID_ARG, PP_ERR_UNSUPPORTED, PP_ERR_WORKSPACE, PP_ERR_HIP = 0, 1, 2, 3, 4
+PP_BF16, PP_F32 = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libppattn.so"
+_lib = None
+
+
+class PPError(RuntimeError):
+    """A non-OK pp_status_t from the library."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m shared_prefix_stream_amd.build` "
+            "(there is no fallback implementation)")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    lib.pp_abi_version.restype = ctypes.c_int
+    lib.pp_abi_version.argtypes = []
+    lib.pp_status_string.restype = ctypes.c_char_p
+    lib.pp_status_string.argtypes = [ctypes.c_int]
+    lib.pp_last_error_message.restype = ctypes.c_char_p
+    lib.pp_last_error_message.argtypes = []
+    lib.pp_attn_workspace_bytes.restype = sz
+    lib.pp_attn_workspace_bytes.argtypes = [i64, i32, i32, i32, ctypes.c_int]
+    for name in ("pp_attn_decode", "pp_attn_decode_batched"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [vp, vp, vp, vp, i64, i32, i32, i32, f32, vp, ctypes.c_int, vp, sz, vp]
+    lib.pp_attn_plan.restype = ctypes.c_int
+    lib.pp_attn_plan.argtypes = [vp, i64, i32, vp, vp, vp, i64, vp]
+    _lib = lib
+    return lib
+
+
+def raw():
+    """The loaded ctypes library (for tests of the C ABI itself)."""
+    return _load()
+
+
+def _check(status: int) -> None:
+    if status != PP_OK:
+        lib = _load()
+        msg = (lib.pp_last_error_message() or b"").decode()
+        base = (lib.pp_status_string(status) or b"").decode()
+        text = f"{base}: {msg}" if msg else base
+        if status in (PP_ERR_INVALID_ARG, PP_ERR_UNSUPPORTED, PP_ERR_WORKSPACE):
+            err = PPError(status, text)
+            raise ValueError(text) from err
+        raise PPError(status, text)
+
+
+def abi_version() -> int:
+    return int(_load().pp_abi_version())
+
+
+def _dtype_code(dtype) -> int:
+    import torch
+
+    if dtype == torch.bfloat16:
+        return PP_BF16
+    if dtype == torch.float32:
+        return PP_F32
+    raise ValueError(f"unsupported dtype {dtype} (bfloat16 or float32)")
+
+
+def workspace_bytes(seq_len: int, P: int, H: int, d: int, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    n = int(_load().pp_attn_workspace_bytes(int(seq_len), int(P), int(H), int(d), code))
+    if n == 0:
+        raise ValueError(f"invalid shape seq_len={seq_len} P={P} H={H} d={d}")
+    return n
+
+
+def _stream_handle(device) -> int:
+    import torch
+
+    return int(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _prepare(q, k_cache, v_cache, stream_id, seq_len, scale, out, workspace):
+    import torch
+
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("stream_id", stream_id)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if q.dim() != 3 or k_cache.dim() != 3 or v_cache.dim() != 3:
+        raise ValueError("q, k_cache, v_cache must be [P,H,d], [T,H,d], [T,H,d]")
+    P, H, d = q.shape
+    if k_cache.shape != v_cache.shape or k_cache.shape[1:] != (H, d):
+        raise ValueError(f"k_cache/v_cache shape {tuple(k_cache.shape)} does not match q {tuple(q.shape)}")
+    if not (q.dtype == k_cache.dtype == v_cache.dtype):
+        raise ValueError("q, k_cache and v_cache must share one dtype")
+    if stream_id.dtype != torch.int32 or stream_id.dim() != 1:
+        raise ValueError("stream_id must be a 1-D int32 tensor")
+    T = k_cache.shape[0]
+    if seq_len is None:
+        seq_len = T
+    if not (1 <= seq_len <= T) or stream_id.shape[0] < seq_len:
+        raise ValueError(f"seq_len={seq_len} must be in [1, {T}] and <= len(stream_id)")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    code = _dtype_code(q.dtype)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_cuda or not out.is_contiguous():
+        raise ValueError("out must be a contiguous GPU tensor shaped and typed like q")
+    need = workspace_bytes(seq_len, P, H, d, code)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    return P, H, d, int(seq_len), float(scale), code, out, workspace
+
+
+def _decode(fn_name, q, k_cache, v_cache, stream_id, seq_len=None, scale=None, out=None, workspace=None):
+    P, H, d, seq_len, scale, code, out, workspace = _prepare(q, k_cache, v_cache, stream_id, seq_len, scale, out,
+                                                             workspace)
+    fn = getattr(_load(), fn_name)
+    st = fn(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), stream_id.data_ptr(), seq_len, P, H, d, scale,
+            out.data_ptr(), code, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+            _stream_handle(q.device))
+    _check(st)
+    return out
+
+
+def pp_attn_decode(q, k_cache, v_cache, stream_id, seq_len: Optional[int] = None, scale: Optional[float] = None,
+                   out=None, workspace=None):
+    """One decode step; the document is read once for all P streams.
+    Enqueued on torch's current stream; returns `out` without synchronising."""
+    return _decode("pp_attn_decode", q, k_cache, v_cache, stream_id, seq_len, scale, out, workspace)
+
+
+def pp_attn_decode_batched(q, k_cache, v_cache, stream_id, seq_len: Optional[int] = None,
+                           scale: Optional[float] = None, out=None, workspace=None):
+    """The same step as P independent per-question requests (the baseline)."""
+    return _decode("pp_attn_decode_batched", q, k_cache, v_cache, stream_id, seq_len, scale, out, workspace)
+
+
+def pp_attn_plan(stream_id, seq_len: int, P: int, tail_capacity: int = 0) -> Tuple:
+    """The device-side integer visibility plan: (doc_len [1], tail counts [P],
+    tail slots [P, tail_capacity]) as int32 GPU tensors."""
+    import torch
+
+    if not isinstance(stream_id, torch.Tensor) or not stream_id.is_cuda or stream_id.dtype != torch.int32:
+        raise ValueError("stream_id must be an int32 GPU tensor")
+    dev = stream_id.device
+    doc_len = torch.empty(1, dtype=torch.int32, device=dev)
+    counts = torch.empty(P, dtype=torch.int32, device=dev)
+    slots = torch.full((P, max(tail_capacity, 1)), -1, dtype=torch.int32, device=dev)
+    st = _load().pp_attn_plan(stream_id.data_ptr(), int(seq_len), int(P), doc_len.data_ptr(), counts.data_ptr(),
+                              slots.data_ptr(), int(tail_capacity), _stream_handle(dev))
+    _check(st)
+    return doc_len, counts, slots[:, :tail_capacity]

@@ -1,0 +1,253 @@
+// Per-stream part of one decode step, and the final merge.
+//
+// After the document, a stream sees only its own slots (its question and
+// its earlier answer tokens) plus any document slot placed later (Parallel
+// Prompting project page, "How it works", item 1).  Instead of testing the
+// stream rule on every slot for every stream -- which makes each stream scan
+// its siblings' answers, the cost the project page's "More results" section
+// blames for the smaller gain on long answers -- each workgroup here
+// compacts the slots its own stream sees (ascending, one workgroup-wide scan
+// per 4096-slot chunk) and gathers only those rows.  A slot's K row over all
+// heads is H*d contiguous elements, so waves read whole 16-byte vectors,
+// coalesced.
+//
+// Workgroup = one stream x a block of heads.  Wave w handles head group
+// (w % HGW) -- GW consecutive heads, i.e. a contiguous GW*d-element slice of
+// each K/V row -- for token substream (w / HGW): substreams take interleaved
+// runs of U list entries, and are merged in substream order at the end.
+// Then the document's split partial states (written by the document kernel
+// or by the per-question baseline) are merged in split order, followed by
+// this stream's own state, and the output row is written.  The fixed merge
+// order makes the result bitwise reproducible.
+#include <math.h>
+
+#include "pp_internal.h"
+
+namespace pp {
+namespace {
+
+constexpr int kTailThreads = 512;  // 8 waves
+constexpr int kTailU = 4;          // list entries per substream step (loads in flight)
+constexpr int kTailNI = 2;         // 16-byte vectors per lane per K row
+
+template <typename T, int D>
+struct TailShape {
+  static constexpr int VEC = 16 / (int)sizeof(T);  // elements per 16-byte vector
+  static constexpr int LPH = D / VEC;              // lanes sharing one head
+  static constexpr int HPI = 64 / LPH;             // heads per wave-wide vector load
+  static constexpr int GW = kTailNI * HPI;         // heads per wave
+};
+
+template <typename T>
+__device__ __forceinline__ void to_f32(const u32x4& w, float* f);
+template <>
+__device__ __forceinline__ void to_f32<uint16_t>(const u32x4& w, float* f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
+    f[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+  }
+}
+template <>
+__device__ __forceinline__ void to_f32<float>(const u32x4& w, float* f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(w[i]);
+}
+
+template <typename T>
+__device__ __forceinline__ u32x4 from_f32(const float* f);
+template <>
+__device__ __forceinline__ u32x4 from_f32<uint16_t>(const float* f) {
+  return u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
+}
+template <>
+__device__ __forceinline__ u32x4 from_f32<float>(const float* f) {
+  return u32x4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3])};
+}
+
+// (M, Ls, A) <- merge with (m2, l2, A2); states with m = -inf are empty.
+template <int VEC>
+__device__ __forceinline__ void merge_state(float& M, float& Ls, float* A, float m2, float l2, const float* A2) {
+  const float Mn = fmaxf(M, m2);
+  if (Mn == -INFINITY) return;
+  const float a = fast_exp2(M - Mn), b = fast_exp2(m2 - Mn);
+  Ls = Ls * a + l2 * b;
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) A[e] = A[e] * a + A2[e] * b;
+  M = Mn;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kTailThreads) void tail_merge_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ sid,
+    int64_t seq_len, int P, int H, float c, const int32_t* __restrict__ doc_len_ptr, int n_splits,
+    const float* __restrict__ part_o, const float2* __restrict__ part_ml, T* __restrict__ out, int HGW) {
+  using S = TailShape<T, D>;
+  constexpr int VEC = S::VEC, LPH = S::LPH, HPI = S::HPI, GW = S::GW;
+  constexpr int NW = kTailThreads / 64;
+  constexpr int RED = kTailNI * (VEC + 2);  // floats per lane in the substream merge
+
+  __shared__ int list[kCollectChunk];
+  __shared__ int scan[NW + 1];
+  __shared__ float red[(NW - 1) * RED * 64];
+
+  const int s = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int NTS = NW / HGW;
+  const int hgl = wave % HGW, ts = wave / HGW;
+  const int hg = blockIdx.y * HGW + hgl;
+  const int64_t row = (int64_t)H * D;
+
+  int head[kTailNI], d0[kTailNI];
+  bool valid[kTailNI];
+#pragma unroll
+  for (int i = 0; i < kTailNI; ++i) {
+    head[i] = hg * GW + i * HPI + lane / LPH;
+    d0[i] = (lane % LPH) * VEC;
+    valid[i] = head[i] < H;
+  }
+
+  float qv[kTailNI][VEC], mm[kTailNI], ll[kTailNI], acc[kTailNI][VEC];
+#pragma unroll
+  for (int i = 0; i < kTailNI; ++i) {
+    u32x4 w = u32x4{0u, 0u, 0u, 0u};
+    if (valid[i]) w = *reinterpret_cast<const u32x4*>(q + ((int64_t)s * H + head[i]) * D + d0[i]);
+    to_f32<T>(w, qv[i]);
+    mm[i] = -INFINITY;
+    ll[i] = 0.f;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[i][e] = 0.f;
+  }
+
+  // ---- own slots (and late document slots), gathered ------------------------
+  int64_t from = *doc_len_ptr;
+  while (from < seq_len) {
+    int64_t next;
+    const int n = collect_visible<kTailThreads>(sid, from, seq_len, s + 1, list, kCollectChunk, &next, scan);
+    for (int base = ts * kTailU; base < n; base += NTS * kTailU) {
+      u32x4 kr[kTailU][kTailNI], vr[kTailU][kTailNI];
+#pragma unroll
+      for (int u = 0; u < kTailU; ++u) {
+        const int j = base + u < n ? list[base + u] : -1;
+#pragma unroll
+        for (int i = 0; i < kTailNI; ++i) {
+          if (j >= 0 && valid[i]) {
+            const int64_t off = (int64_t)j * row + (int64_t)head[i] * D + d0[i];
+            kr[u][i] = *reinterpret_cast<const u32x4*>(k + off);
+            vr[u][i] = *reinterpret_cast<const u32x4*>(v + off);
+          } else {
+            kr[u][i] = u32x4{0u, 0u, 0u, 0u};
+            vr[u][i] = u32x4{0u, 0u, 0u, 0u};
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kTailU; ++u) {
+        if (base + u >= n) break;  // uniform across the workgroup
+#pragma unroll
+        for (int i = 0; i < kTailNI; ++i) {
+          float kf[VEC], vf[VEC];
+          to_f32<T>(kr[u][i], kf);
+          to_f32<T>(vr[u][i], vf);
+          float dot = 0.f;
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) dot = fmaf(qv[i][e], kf[e], dot);
+          dot = group_sum<LPH>(dot);
+          const float t = dot * c;
+          const float mn = fmaxf(mm[i], t);
+          const float alpha = fast_exp2(mm[i] - mn);
+          const float p = fast_exp2(t - mn);
+          ll[i] = ll[i] * alpha + p;
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) acc[i][e] = fmaf(p, vf[e], acc[i][e] * alpha);
+          mm[i] = mn;
+        }
+      }
+    }
+    from = next;
+    __syncthreads();  // list[] is refilled by the next round
+  }
+
+  // ---- merge token substreams (fixed order 0, 1, ..., NTS-1) -----------------
+  if (ts > 0) {
+    float* r = red + (size_t)((ts - 1) * HGW + hgl) * RED * 64;
+#pragma unroll
+    for (int i = 0; i < kTailNI; ++i) {
+      r[(i * (VEC + 2) + 0) * 64 + lane] = mm[i];
+      r[(i * (VEC + 2) + 1) * 64 + lane] = ll[i];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) r[(i * (VEC + 2) + 2 + e) * 64 + lane] = acc[i][e];
+    }
+  }
+  __syncthreads();
+  if (ts != 0 || hg * GW >= H) return;
+  for (int t2 = 1; t2 < NTS; ++t2) {
+    const float* r = red + (size_t)((t2 - 1) * HGW + hgl) * RED * 64;
+#pragma unroll
+    for (int i = 0; i < kTailNI; ++i) {
+      float a2[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) a2[e] = r[(i * (VEC + 2) + 2 + e) * 64 + lane];
+      merge_state<VEC>(mm[i], ll[i], acc[i], r[(i * (VEC + 2)) * 64 + lane], r[(i * (VEC + 2) + 1) * 64 + lane], a2);
+    }
+  }
+
+  // ---- merge document splits in order, then this stream's own state ---------
+#pragma unroll
+  for (int i = 0; i < kTailNI; ++i) {
+    if (!valid[i]) continue;
+    float M = -INFINITY, Ls = 0.f, A[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) A[e] = 0.f;
+#pragma unroll 4
+    for (int sp = 0; sp < n_splits; ++sp) {
+      const int64_t sh = ((int64_t)sp * P + s) * H + head[i];
+      const float2 ml = part_ml[sh];
+      float o2[VEC];
+      const float* src = part_o + sh * D + d0[i];
+#pragma unroll
+      for (int e = 0; e < VEC; e += 4) {
+        const float4 x = *reinterpret_cast<const float4*>(src + e);
+        o2[e] = x.x;
+        o2[e + 1] = x.y;
+        o2[e + 2] = x.z;
+        o2[e + 3] = x.w;
+      }
+      merge_state<VEC>(M, Ls, A, ml.x, ml.y, o2);
+    }
+    merge_state<VEC>(M, Ls, A, mm[i], ll[i], acc[i]);
+    float res[VEC];
+    const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) res[e] = Ls > 0.f ? A[e] * inv : 0.f;
+    *reinterpret_cast<u32x4*>(out + ((int64_t)s * H + head[i]) * D + d0[i]) = from_f32<T>(res);
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_tail_t(int n_splits, const void* q, const void* k, const void* v, const int32_t* sid,
+                         int64_t seq_len, int P, int H, float c, const Workspace& ws, void* out, hipStream_t stream) {
+  using S = TailShape<T, D>;
+  const int nhg = (H + S::GW - 1) / S::GW;
+  int hgw = 1;
+  while (hgw * 2 <= nhg && hgw * 2 <= kTailThreads / 64) hgw *= 2;
+  const dim3 grid(P, (nhg + hgw - 1) / hgw);
+  tail_merge_kernel<T, D><<<grid, kTailThreads, 0, stream>>>(
+      static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), sid, seq_len, P, H, c, ws.doc_len,
+      n_splits, ws.part_o, ws.part_ml, static_cast<T*>(out), hgw);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_tail_merge(int n_splits, const void* q, const void* k, const void* v, const int32_t* sid,
+                             int64_t seq_len, int P, int H, int d, pp_dtype_t dtype, float c, const Workspace& ws,
+                             void* out, hipStream_t stream) {
+  if (dtype == PP_BF16)
+    return d == 128 ? launch_tail_t<uint16_t, 128>(n_splits, q, k, v, sid, seq_len, P, H, c, ws, out, stream)
+                    : launch_tail_t<uint16_t, 64>(n_splits, q, k, v, sid, seq_len, P, H, c, ws, out, stream);
+  return d == 128 ? launch_tail_t<float, 128>(n_splits, q, k, v, sid, seq_len, P, H, c, ws, out, stream)
+                  : launch_tail_t<float, 64>(n_splits, q, k, v, sid, seq_len, P, H, c, ws, out, stream);
+}
+
+}  // namespace pp

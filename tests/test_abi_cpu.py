@@ -1,0 +1,110 @@
+"""The C ABI on a machine without a GPU: the library loads, exports every
+symbol include/ppattn.h declares, and rejects bad arguments on the host
+before any HIP call (only fake, never-dereferenced pointers are passed)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import shared_prefix_stream_amd as pp
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "ppattn.h")
+
+# fake device addresses, 16-byte aligned and far apart
+Q, K, V, SID, OUT, WS = (0x10000000 * i for i in range(1, 7))
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pp_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = pp.raw()
+    names = _declared_functions()
+    assert set(names) >= {"pp_attn_decode", "pp_attn_decode_batched", "pp_attn_workspace_bytes", "pp_attn_plan",
+                          "pp_abi_version", "pp_status_string", "pp_last_error_message"}
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in ppattn.h but not exported"
+
+
+def test_abi_version_and_status_strings():
+    lib = pp.raw()
+    assert pp.abi_version() == 1
+    for code in range(5):
+        assert lib.pp_status_string(code).decode().startswith("PP_")
+    assert b"unknown" in lib.pp_status_string(99)
+
+
+def _decode(fn="pp_attn_decode", q=Q, k=K, v=V, sid=SID, seq_len=1000, P=8, H=4, d=128, scale=0.088, out=OUT,
+            dtype=pp.PP_BF16, ws=WS, ws_bytes=None, stream=None):
+    lib = pp.raw()
+    if ws_bytes is None:
+        ws_bytes = lib.pp_attn_workspace_bytes(seq_len, P, H, d, dtype) if d in (64, 128) and dtype in (0, 1) else 1 << 20
+    return getattr(lib, fn)(q, k, v, sid, seq_len, P, H, d, scale, out, dtype, ws, ws_bytes, stream)
+
+
+@pytest.mark.parametrize("fn", ["pp_attn_decode", "pp_attn_decode_batched"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(P=0), pp.PP_ERR_INVALID_ARG),
+    (dict(P=70000), pp.PP_ERR_INVALID_ARG),
+    (dict(H=0), pp.PP_ERR_INVALID_ARG),
+    (dict(seq_len=0), pp.PP_ERR_INVALID_ARG),
+    (dict(seq_len=(1 << 30) + 1), pp.PP_ERR_INVALID_ARG),
+    (dict(q=None), pp.PP_ERR_INVALID_ARG),
+    (dict(k=None), pp.PP_ERR_INVALID_ARG),
+    (dict(v=None), pp.PP_ERR_INVALID_ARG),
+    (dict(sid=None), pp.PP_ERR_INVALID_ARG),
+    (dict(out=None), pp.PP_ERR_INVALID_ARG),
+    (dict(scale=math.inf), pp.PP_ERR_INVALID_ARG),
+    (dict(scale=math.nan), pp.PP_ERR_INVALID_ARG),
+    (dict(q=Q + 8), pp.PP_ERR_INVALID_ARG),
+    (dict(sid=SID + 4), pp.PP_ERR_INVALID_ARG),
+    (dict(out=Q + 64), pp.PP_ERR_INVALID_ARG),       # out overlaps q
+    (dict(out=K + 4096), pp.PP_ERR_INVALID_ARG),     # out overlaps k_cache
+    (dict(out=WS + 256), pp.PP_ERR_INVALID_ARG),     # out overlaps workspace
+    (dict(ws=V + 256), pp.PP_ERR_INVALID_ARG),       # workspace overlaps v_cache
+    (dict(d=96), pp.PP_ERR_UNSUPPORTED),
+    (dict(d=256), pp.PP_ERR_UNSUPPORTED),
+    (dict(dtype=7), pp.PP_ERR_UNSUPPORTED),
+    (dict(ws=None), pp.PP_ERR_WORKSPACE),
+    (dict(ws_bytes=1024), pp.PP_ERR_WORKSPACE),
+])
+def test_host_validation(fn, kw, status):
+    assert _decode(fn, **kw) == status
+    assert pp.raw().pp_last_error_message().decode() != ""
+
+
+def test_workspace_bytes():
+    lib = pp.raw()
+    assert lib.pp_attn_workspace_bytes(0, 8, 4, 128, pp.PP_BF16) == 0
+    assert lib.pp_attn_workspace_bytes(100, 8, 4, 96, pp.PP_BF16) == 0
+    assert lib.pp_attn_workspace_bytes(100, 8, 4, 128, 5) == 0
+    # at least one split of partial states (m, l, d floats) per (stream, head)
+    for (T, P, H, d) in [(304, 4, 4, 64), (31488, 256, 32, 128), (82000, 512, 32, 128), (1, 1, 1, 64)]:
+        n = lib.pp_attn_workspace_bytes(T, P, H, d, pp.PP_BF16)
+        assert n >= P * H * (d + 2) * 4 + 256
+    assert lib.pp_last_error_message() == b""
+
+
+def test_plan_validation():
+    lib = pp.raw()
+    assert lib.pp_attn_plan(None, 10, 2, OUT, WS, K, 4, None) == pp.PP_ERR_INVALID_ARG
+    assert lib.pp_attn_plan(SID, 0, 2, OUT, WS, K, 4, None) == pp.PP_ERR_INVALID_ARG
+    assert lib.pp_attn_plan(SID, 10, 0, OUT, WS, K, 4, None) == pp.PP_ERR_INVALID_ARG
+    assert lib.pp_attn_plan(SID, 10, 2, None, WS, K, 4, None) == pp.PP_ERR_INVALID_ARG
+    assert lib.pp_attn_plan(SID, 10, 2, OUT, None, K, 4, None) == pp.PP_ERR_INVALID_ARG
+    assert lib.pp_attn_plan(SID, 10, 2, OUT, WS, None, 4, None) == pp.PP_ERR_INVALID_ARG
+    assert lib.pp_attn_plan(SID, 10, 2, OUT, WS, K, -1, None) == pp.PP_ERR_INVALID_ARG
+    assert lib.pp_attn_plan(SID + 4, 10, 2, OUT, WS, K, 4, None) == pp.PP_ERR_INVALID_ARG
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+
+    q = torch.zeros(2, 1, 64)
+    with pytest.raises(ValueError):
+        pp.pp_attn_decode(q, q, q, torch.zeros(2, dtype=torch.int32))

@@ -1,0 +1,181 @@
+"""GPU tests of the method's properties, through the C ABI:
+isolation between streams (bit-identical), run-to-run determinism, the
+integer visibility plan (bit-exact vs the oracle), layouts the canonical
+generator does not produce, degenerate cases, and stream semantics."""
+import numpy as np
+import pytest
+import torch
+
+import shared_prefix_stream_amd as pp
+from oracle import tail_lists
+from tests.gpu_helpers import assert_close, reference, run, say, to_gpu
+from workloads import make_case, permute_tail
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(seed, P=6, H=4, D=128, doc=700, dtype=torch.bfloat16, qmax=12, amax=8, **kw):
+    rng = np.random.default_rng(seed)
+    return make_case(H, D, doc, rng.integers(1, qmax + 1, P).tolist(), rng.integers(0, amax + 1, P).tolist(),
+                     dtype=dtype, seed=seed, name=f"sem_p{P}_doc{doc}_s{seed}", **kw)
+
+
+# ---------------------------------------------------------------- isolation ---
+
+@pytest.mark.parametrize("entry", ["decode", "batched"])
+@pytest.mark.parametrize("bad", ["finite", "inf", "nan"])
+def test_other_streams_cannot_reach_a_stream(entry, bad):
+    case = _case(1, P=5)
+    base = run(case, entry).cpu()
+    for s in range(case.P):
+        k, v = case.k.clone(), case.v.clone()
+        for o in range(case.P):
+            if o == s:
+                continue
+            idx = torch.from_numpy(case.own_slots[o])
+            if bad == "finite":
+                k[idx] = (k[idx].float() * 3 + 1).to(k.dtype)
+                v[idx] = (v[idx].float() - 2).to(v.dtype)
+            else:
+                val = float("inf") if bad == "inf" else float("nan")
+                k[idx] = val
+                v[idx] = val
+        args = [case.q.cuda(), k.cuda(), v.cuda(), case.stream_id.cuda()]
+        out = run(case, entry, gpu_args=args).cpu()
+        assert torch.equal(out[s].view(torch.int16), base[s].view(torch.int16)), f"stream {s} changed"
+
+
+# ------------------------------------------------------------- determinism ---
+
+@pytest.mark.parametrize("entry", ["decode", "batched"])
+def test_bitwise_reproducible(entry):
+    case = _case(2, P=40, H=8, doc=3000)
+    args = to_gpu(case)
+    first = run(case, entry, gpu_args=args).clone()
+    for _ in range(4):
+        again = run(case, entry, gpu_args=args)
+        assert torch.equal(first.view(torch.int16), again.view(torch.int16))
+
+
+# -------------------------------------------------------- integer plan (a1) ---
+
+def _plan_check(ids_np, seq_len, P, cap=8192):
+    sid = torch.from_numpy(np.ascontiguousarray(ids_np, dtype=np.int32)).cuda()
+    say(f"  gpu: pp_attn_plan T={seq_len} P={P}")
+    doc_len, counts, slots = pp.pp_attn_plan(sid, seq_len, P, cap)
+    torch.cuda.synchronize()
+    d_ref, lists = tail_lists(ids_np, seq_len, P)
+    assert int(doc_len.item()) == d_ref
+    counts = counts.cpu().numpy()
+    slots = slots.cpu().numpy()
+    for s in range(P):
+        assert counts[s] == len(lists[s]), f"stream {s}"
+        n = min(len(lists[s]), cap)
+        assert np.array_equal(slots[s, :n], lists[s][:n]), f"stream {s}"
+
+
+def test_plan_canonical_and_permuted():
+    case = _case(3, P=37, doc=5000, qmax=40, amax=30)
+    _plan_check(case.stream_id.numpy(), case.seq_len, case.P)
+    pc = permute_tail(case, 4)
+    _plan_check(pc.stream_id.numpy(), pc.seq_len, pc.P)
+
+
+def test_plan_junk_ids_late_document_and_no_document():
+    rng = np.random.default_rng(5)
+    P = 9
+    ids = np.concatenate([np.zeros(300), rng.integers(-3, P + 4, 7000)]).astype(np.int32)
+    ids[rng.integers(300, 7300, 50)] = 0  # document slots after the prefix
+    _plan_check(ids, len(ids), P)
+    _plan_check(ids, 4000, P)  # seq_len inside the buffer (not a multiple of 4 away from anything)
+    _plan_check(ids[300:].copy(), 5001, P)  # first slot not a document slot: doc_len 0
+
+
+def test_plan_all_document_and_many_own_slots():
+    _plan_check(np.zeros(10001, dtype=np.int32), 10001, 3)
+    # one stream owning more slots than one 4096-slot compaction chunk holds
+    ids = np.concatenate([np.zeros(17), np.ones(9000), np.full(3, 2)]).astype(np.int32)
+    _plan_check(ids, len(ids), 2, cap=10000)
+
+
+# ---------------------------------------------------------- layout variants ---
+
+@pytest.mark.parametrize("entry", ["decode", "batched"])
+def test_permuted_tail_layout(entry):
+    case = permute_tail(_case(6, P=11, doc=900), 7)
+    assert_close(run(case, entry), reference(case), what=case.name)
+
+
+@pytest.mark.parametrize("entry", ["decode", "batched"])
+def test_late_document_slots_and_foreign_ids(entry):
+    case = _case(8, P=6, doc=400)
+    rng = np.random.default_rng(9)
+    sid = case.stream_id.clone()
+    tail = np.arange(case.doc_len, case.seq_len)
+    pick = rng.choice(tail, 12, replace=False)
+    sid[torch.from_numpy(pick[:6])] = 0            # visible to every stream
+    sid[torch.from_numpy(pick[6:9])] = -1          # the page's document id: not this encoding's
+    sid[torch.from_numpy(pick[9:])] = case.P + 3   # no such stream
+    case.stream_id = sid
+    assert_close(run(case, entry), reference(case), what="late-doc/foreign ids")
+
+
+@pytest.mark.parametrize("entry", ["decode", "batched"])
+def test_only_first_seq_len_slots_read(entry):
+    case = _case(10, P=4, doc=500, extra_capacity=333)  # slots past seq_len hold NaN
+    assert_close(run(case, entry), reference(case), what="extra capacity")
+
+
+# ------------------------------------------------------------ degenerate ---
+
+@pytest.mark.parametrize("entry", ["decode", "batched"])
+def test_empty_visible_set_gives_zeros(entry):
+    # no document at all; stream 1 owns nothing
+    case = make_case(2, 128, 0, [3, 0, 2], [1, 0, 2], seed=11, name="no-doc")
+    out = run(case, entry).cpu()
+    assert torch.equal(out[1], torch.zeros_like(out[1]))
+    assert_close(out, reference(case), what="no-doc")
+
+
+@pytest.mark.parametrize("entry", ["decode", "batched"])
+def test_single_visible_key_returns_its_value(entry):
+    case = make_case(4, 128, 1, [0, 0, 0], [0, 0, 0], seed=12, name="doc1")
+    out = run(case, entry).cpu()
+    for s in range(3):
+        assert torch.equal(out[s].view(torch.int16), case.v[0].view(torch.int16))
+
+
+@pytest.mark.parametrize("entry", ["decode", "batched"])
+def test_p1_is_causal_attention(entry):
+    # one stream, its current token's K/V appended last: plain causal attention
+    case = make_case(4, 128, 2000, [30], [9], seed=13, name="p1")
+    assert_close(run(case, entry), reference(case), what="P=1")
+
+
+@pytest.mark.parametrize("entry", ["decode", "batched"])
+def test_peaked_softmax_outliers(entry):
+    case = _case(14, P=8, doc=2000, outlier_frac=0.01, outlier_mult=50.0)
+    assert_close(run(case, entry), reference(case), what="outliers")
+
+
+# -------------------------------------------------------------- streams ---
+
+def test_runs_on_a_side_stream_without_host_sync():
+    case = _case(15, P=12, doc=1200)
+    args = to_gpu(case)
+    side = torch.cuda.Stream()
+    say("  gpu: decode on a side stream")
+    with torch.cuda.stream(side):
+        out = pp.pp_attn_decode(*args, seq_len=case.seq_len, scale=case.scale)
+        out2 = pp.pp_attn_decode_batched(*args, seq_len=case.seq_len, scale=case.scale)
+    side.synchronize()
+    ref = reference(case)
+    assert_close(out, ref, what="side stream")
+    assert_close(out2, ref, what="side stream batched")
+
+
+def test_decode_and_batched_agree():
+    case = _case(16, P=33, H=8, doc=4100)
+    a = run(case, "decode").double().cpu().numpy()
+    b = run(case, "batched").double().cpu().numpy()
+    assert np.abs(a - b).max() <= 2e-2
