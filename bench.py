@@ -1,0 +1,334 @@
+#!/usr/bin/env python3
+"""Benchmark of one decode step of Parallel Prompting attention on one MI355X.
+
+A step is one call of pp_attn_decode: the visibility plan, the document part
+(read once for all P streams, MFMA), the per-stream own-slot gather and the
+merge.  Workload (default): CodeLlama-7B attention shape, H=32 heads of
+d=128, bf16, a 16384-token document, P=256 streams with questions uniform
+8-48 tokens and 31 prior answer tokens each, answers interleaved by step,
+seeded N(0,1) inputs resident in HBM before timing starts.
+
+Prints ONE JSON line (the headline number is answer tokens per second of
+one layer's attention) with: effective KV bandwidth and its fraction of the
+8 TB/s HBM peak, the per-kernel durations measured with HIP events recorded
+by the library on the stream its kernels run on, the roofline of the
+dominant kernel, the per-question baseline's time on the same inputs, and
+the fp64 CPU oracle timed on a bounded sample of streams.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+    python bench.py --copy-calibration   # plain 1 GiB copy, to scale PMC byte counters
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "answer tok/s & effective doc-KV GB/s (% HBM peak), doc=16k P=256 H=32 d=128"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_digest() -> str:
+    """Hash of the HIP sources: PMC byte counts in profiles/ are only used
+    while the kernels are unchanged since they were taken."""
+    csrc = os.path.join(ROOT, "shared_prefix_stream_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_pmc_traffic(stage: str, workload: str):
+    """HBM bytes per launch from profiles/pmc_<stage>_<workload>.txt
+    (FETCH_SIZE and WRITE_SIZE in KiB per dispatch, each scaled by the copy
+    calibration factor), or None if absent or taken on other kernel sources."""
+    path = os.path.join(PROFILES, f"pmc_{stage}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def step_bytes(case):
+    """Algorithmic bytes: the document's K/V once, each stream's own slots
+    once (read by their owner only), Q, out and the stream ids."""
+    es = case.q.element_size()
+    row = case.H * case.D * es
+    tail = sum(len(o) for o in case.own_slots)
+    return {
+        "doc_kv": 2 * case.doc_len * row,
+        "tail_kv": 2 * tail * row,
+        "q": case.P * row,
+        "out": case.P * row,
+        "ids": 4 * case.seq_len,
+        "tail_slots": tail,
+        "doc_flops": 4 * case.D * case.H * case.P * case.doc_len,
+        "tail_flops": 4 * case.D * case.H * tail,
+    }
+
+
+def cpu_baseline(case, target_s: float):
+    """The fp64 oracle as it stands, timed on a bounded sample of streams of
+    the same inputs (all heads each)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import oracle_decode
+
+    ids = case.stream_id.numpy()
+    rng = np.random.default_rng(0)
+    order = rng.permutation(case.P).tolist()
+
+    def timed(n):
+        t = time.perf_counter()
+        oracle_decode(case.q, case.k, case.v, ids, case.seq_len, case.scale, streams=order[:n])
+        return time.perf_counter() - t
+
+    # each call also converts the cache to fp64: fit t(n) = a + b*n from two
+    # small calls, then size the timed sample to about target_s
+    n1, n2 = 2, min(case.P, 8)
+    t1, t2 = timed(n1), timed(n2)
+    b = max((t2 - t1) / max(n2 - n1, 1), 1e-4)
+    a = max(t1 - b * n1, 0.0)
+    n = int(max(n2, min(case.P, (target_s - a) / b)))
+    dt = timed(n)
+    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    return {
+        "value": n / dt,
+        "unit": "answer tok/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{n} of {case.P} streams x all {case.H} heads of the same step, fp64 NumPy, {dt:.1f} s "
+                  f"(includes the oracle's fp64 conversion of the KV cache)",
+        "seconds": dt,
+        "cpu_model": _cpu_model(),
+    }
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def copy_calibration(steps: int):
+    import torch
+
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    print(json.dumps({"copy_bytes": n, "read_bytes": n, "write_bytes": n, "ms": ms,
+                      "gbs_read_plus_write": 2 * n / ms / 1e6}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="codellama7b_doc16k_p256")
+    ap.add_argument("--seed", type=int, default=1002)
+    ap.add_argument("--baseline-steps", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-batched", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}): the decode step of one "
+              "request runs on one MI355X; multi-GPU sharding is not part of this library.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import shared_prefix_stream_amd as pp
+    from workloads import named_workload
+
+    if args.copy_calibration:
+        copy_calibration(args.steps)
+        return
+
+    dev = torch.device("cuda:0")
+    log(f"bench: generating {args.workload} seed {args.seed}")
+    case = named_workload(args.workload, seed=args.seed)
+    q, k, v, sid = (t.to(dev) for t in (case.q, case.k, case.v, case.stream_id))
+    out = torch.empty_like(q)
+    ws = torch.empty(pp.workspace_bytes(case.seq_len, case.P, case.H, case.D, q.dtype), dtype=torch.uint8, device=dev)
+    by = step_bytes(case)
+
+    def step():
+        pp.pp_attn_decode(q, k, v, sid, seq_len=case.seq_len, scale=case.scale, out=out, workspace=ws)
+
+    # ---- headline: K back-to-back steps, inputs resident in HBM --------------
+    log(f"bench: warmup {args.warmup}, timed {args.steps}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - w0) * 1e3 / args.steps
+    ms = e0.elapsed_time(e1) / args.steps
+    t_s = ms / 1e3
+
+    # ---- per-kernel durations from events the library records on its stream --
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    handles = [e.cuda_event for e in evs]
+    stage_ms = [0.0, 0.0, 0.0]
+    n_prof = max(5, min(args.steps, 50))
+    for _ in range(n_prof):
+        pp.pp_attn_decode_profiled(handles, q, k, v, sid, seq_len=case.seq_len, scale=case.scale, out=out,
+                                   workspace=ws)
+        evs[3].synchronize()
+        for i in range(3):
+            stage_ms[i] += evs[i].elapsed_time(evs[i + 1])
+    stage_us = {name: stage_ms[i] / n_prof * 1e3 for i, name in enumerate(pp.PROFILE_STAGES)}
+
+    # ---- cold steps: 1 GiB written between steps evicts L2 and the MALL -------
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cold = []
+    for _ in range(min(args.steps, 20)):
+        flush.fill_(1)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        step()
+        b.record()
+        torch.cuda.synchronize()
+        cold.append(a.elapsed_time(b))
+    del flush
+    cold.sort()
+    cold_ms = cold[len(cold) // 2]
+
+    # ---- per-question baseline on the same inputs -----------------------------
+    batched = None
+    if not args.no_batched:
+        log("bench: per-question baseline")
+        outb = torch.empty_like(q)
+        for _ in range(2):
+            pp.pp_attn_decode_batched(q, k, v, sid, seq_len=case.seq_len, scale=case.scale, out=outb, workspace=ws)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.baseline_steps):
+            pp.pp_attn_decode_batched(q, k, v, sid, seq_len=case.seq_len, scale=case.scale, out=outb, workspace=ws)
+        b.record()
+        torch.cuda.synchronize()
+        bms = a.elapsed_time(b) / args.baseline_steps
+        batched = {"ms_per_step": bms, "speedup_of_decode": bms / ms,
+                   "logical_doc_reads_gb": by["doc_kv"] * case.P / 1e9,
+                   "max_abs_diff_vs_decode": float((outb.float() - out.float()).abs().max())}
+
+    # ---- numbers ----------------------------------------------------------------
+    kv = by["doc_kv"] + by["tail_kv"]
+    kv_gbs = kv / t_s / 1e9
+    doc_gbs = by["doc_kv"] / t_s / 1e9
+    stage_bytes = {
+        "plan": by["ids"],
+        "document": by["doc_kv"] + by["q"],
+        "own_slots_merge": by["tail_kv"] + by["q"] + by["out"] + by["ids"],
+    }
+    kernels = {}
+    for name, us in stage_us.items():
+        gbs = stage_bytes[name] / (us * 1e-6) / 1e9 if us > 0 else 0.0
+        kernels[name] = {"us": us, "algorithmic_bytes": stage_bytes[name], "gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
+    doc_tflops = by["doc_flops"] / (stage_us["document"] * 1e-6) / 1e12
+    kernels["document"]["mfma_tflops"] = doc_tflops
+    kernels["document"]["mfma_frac"] = doc_tflops / MFMA_BF16_PEAK_TFLOPS
+    dom = max(stage_us, key=stage_us.get)
+    dom_traffic = read_pmc_traffic(dom, args.workload)
+    roofline = {
+        "bound": "hbm",
+        "kernel": dom,
+        "achieved": kernels[dom]["gbs"],
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": kernels[dom]["gbs"] / HBM_PEAK_GBS,
+        "traffic": dom_traffic,
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: CPU oracle baseline")
+        cpu = cpu_baseline(case, args.cpu_seconds)
+
+    result = {
+        "metric": METRIC,
+        "value": case.P / t_s,
+        "unit": "answer tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) Q/K/V rounded to bf16, canonical layout (document, questions, answers "
+                "interleaved by step); one layer's attention, no model weights",
+        "config": {"workload": args.workload, "H": case.H, "d": case.D, "doc_len": case.doc_len, "P": case.P,
+                   "seq_len": case.seq_len, "tail_slots": by["tail_slots"], "seed": args.seed},
+        "steps_per_s": 1 / t_s,
+        "wall_ms_per_step": wall_ms,
+        "cold_ms_per_step": cold_ms,
+        "effective_kv_gbs": kv_gbs,
+        "effective_kv_hbm_frac": kv_gbs / HBM_PEAK_GBS,
+        "doc_kv_gbs": doc_gbs,
+        "doc_kv_hbm_frac": doc_gbs / HBM_PEAK_GBS,
+        "step_algorithmic_bytes": kv + by["q"] + by["out"] + by["ids"],
+        "step_flops": by["doc_flops"] + by["tail_flops"],
+        "kernels": kernels,
+        "roofline": roofline,
+        "batched_baseline": batched,
+        "cpu_baseline": cpu,
+        "kernel_source_digest": kernel_source_digest(),
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

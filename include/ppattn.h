@@ -123,19 +123,38 @@ pp_status_t pp_attn_decode_batched(const void* q, const void* k_cache, const voi
                                    int32_t d, float scale, void* out, pp_dtype_t dtype,
                                    void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* Profiling variant of pp_attn_decode (batched == 0) or pp_attn_decode_batched
+ * (batched != 0): identical arguments, contract and results, and it also
+ * records caller-created hipEvent_t events on hip_stream around its kernel
+ * launches, so each stage can be timed with hipEventElapsedTime on the stream
+ * the kernels actually run on.  events[0] is recorded before the first
+ * launch and events[i] right after the i-th; the stages, in launch order,
+ * are: visibility plan, document part, own-slot gather + merge.  Needs
+ * n_events >= PP_PROFILE_EVENTS (else PP_ERR_INVALID_ARG); a failed event
+ * record is PP_ERR_HIP. */
+#define PP_PROFILE_EVENTS 4
+pp_status_t pp_attn_decode_profiled(int32_t batched, const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* stream_id, int64_t seq_len, int32_t P, int32_t H, int32_t d,
+                                    float scale, void* out, pp_dtype_t dtype, void* workspace,
+                                    size_t workspace_bytes, void* hip_stream, void* const* events,
+                                    int32_t n_events);
+
 /* The integer visibility plan that both entry points evaluate on the device,
- * exposed for inspection.  Writes, on `hip_stream`:
+ * exposed for inspection (the same device code as the attention kernels).
+ * Writes, on `hip_stream`:
  *   doc_len_out[0]      length of the leading run of id-0 slots (<= seq_len)
  *   tail_count_out[s]   number of slots j >= doc_len visible to stream s
  *                       (its own slots and later id-0 slots)
  *   tail_slots_out[s*tail_capacity + i]  the first min(count, tail_capacity)
  *                       of those slots, ascending
  * All three are caller-owned device buffers (int32; tail_slots_out may be
- * NULL when tail_capacity is 0).  [Project page, "How it works", item 1.]
- * Errors as above (PP_ERR_INVALID_ARG for null/invalid arguments). */
+ * NULL when tail_capacity is 0); `workspace` is caller-owned device scratch of
+ * at least PP_PLAN_WORKSPACE_BYTES.  [Project page, "How it works", item 1.]
+ * Errors as above. */
+#define PP_PLAN_WORKSPACE_BYTES 512
 pp_status_t pp_attn_plan(const int32_t* stream_id, int64_t seq_len, int32_t P,
                          int32_t* doc_len_out, int32_t* tail_count_out, int32_t* tail_slots_out,
-                         int64_t tail_capacity, void* hip_stream);
+                         int64_t tail_capacity, void* workspace, size_t workspace_bytes, void* hip_stream);
 
 #ifdef __cplusplus
 }

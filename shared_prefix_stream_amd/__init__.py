@@ -29,6 +29,8 @@ __all__ = [
     "pp_attn_decode",
     "pp_attn_decode_batched",
     "pp_attn_plan",
+    "pp_attn_decode_profiled",
+    "PROFILE_STAGES",
     "PP_OK",
     "PP_ERR_INVALID_ARG",
     "PP_ERR_UNSUPPORTED",
@@ -39,6 +41,7 @@ __all__ = [
 ]
 
 PP_OK, PP_ERR_INVALID_ARG, PP_ERR_UNSUPPORTED, PP_ERR_WORKSPACE, PP_ERR_HIP = 0, 1, 2, 3, 4
+PP_PLAN_WORKSPACE_BYTES = 512
 PP_BF16, PP_F32 = 0, 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -81,8 +84,11 @@ def _load():
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [vp, vp, vp, vp, i64, i32, i32, i32, f32, vp, ctypes.c_int, vp, sz, vp]
+    lib.pp_attn_decode_profiled.restype = ctypes.c_int
+    lib.pp_attn_decode_profiled.argtypes = [i32, vp, vp, vp, vp, i64, i32, i32, i32, f32, vp, ctypes.c_int, vp, sz, vp,
+                                            ctypes.POINTER(vp), i32]
     lib.pp_attn_plan.restype = ctypes.c_int
-    lib.pp_attn_plan.argtypes = [vp, i64, i32, vp, vp, vp, i64, vp]
+    lib.pp_attn_plan.argtypes = [vp, i64, i32, vp, vp, vp, i64, vp, sz, vp]
     _lib = lib
     return lib
 
@@ -191,6 +197,26 @@ def pp_attn_decode_batched(q, k_cache, v_cache, stream_id, seq_len: Optional[int
     return _decode("pp_attn_decode_batched", q, k_cache, v_cache, stream_id, seq_len, scale, out, workspace)
 
 
+PP_PROFILE_EVENTS = 4
+PROFILE_STAGES = ("plan", "document", "own_slots_merge")
+
+
+def pp_attn_decode_profiled(events, q, k_cache, v_cache, stream_id, seq_len: Optional[int] = None,
+                            scale: Optional[float] = None, out=None, workspace=None, batched: bool = False):
+    """pp_attn_decode (or the batched baseline) with raw hipEvent_t handles
+    recorded around each kernel launch: events[0] before the plan kernel,
+    events[i] after the i-th of (plan, document, own-slot gather + merge)."""
+    P, H, d, seq_len, scale, code, out, workspace = _prepare(q, k_cache, v_cache, stream_id, seq_len, scale, out,
+                                                             workspace)
+    arr = (ctypes.c_void_p * len(events))(*events)
+    st = _load().pp_attn_decode_profiled(
+        1 if batched else 0, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), stream_id.data_ptr(), seq_len, P,
+        H, d, scale, out.data_ptr(), code, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        _stream_handle(q.device), arr, len(events))
+    _check(st)
+    return out
+
+
 def pp_attn_plan(stream_id, seq_len: int, P: int, tail_capacity: int = 0) -> Tuple:
     """The device-side integer visibility plan: (doc_len [1], tail counts [P],
     tail slots [P, tail_capacity]) as int32 GPU tensors."""
@@ -202,7 +228,8 @@ def pp_attn_plan(stream_id, seq_len: int, P: int, tail_capacity: int = 0) -> Tup
     doc_len = torch.empty(1, dtype=torch.int32, device=dev)
     counts = torch.empty(P, dtype=torch.int32, device=dev)
     slots = torch.full((P, max(tail_capacity, 1)), -1, dtype=torch.int32, device=dev)
+    ws = torch.empty(PP_PLAN_WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
     st = _load().pp_attn_plan(stream_id.data_ptr(), int(seq_len), int(P), doc_len.data_ptr(), counts.data_ptr(),
-                              slots.data_ptr(), int(tail_capacity), _stream_handle(dev))
+                              slots.data_ptr(), int(tail_capacity), ws.data_ptr(), ws.numel(), _stream_handle(dev))
     _check(st)
     return doc_len, counts, slots[:, :tail_capacity]

@@ -90,7 +90,7 @@ enum class Path { kParallel, kBatched };
 
 pp_status_t decode_impl(Path path, const void* q, const void* k, const void* v, const int32_t* sid, int64_t seq_len,
                         int32_t P, int32_t H, int32_t d, float scale, void* out, pp_dtype_t dtype, void* workspace,
-                        size_t workspace_bytes, void* hip_stream) {
+                        size_t workspace_bytes, void* hip_stream, void* const* events = nullptr) {
   pp_status_t st = check_shape(seq_len, P, H, d, dtype);
   if (st != PP_OK) return st;
   if (!q || !k || !v || !sid || !out) return fail(PP_ERR_INVALID_ARG, "null q, k_cache, v_cache, stream_id or out");
@@ -117,13 +117,21 @@ pp_status_t decode_impl(Path path, const void* q, const void* k, const void* v, 
   const int n_splits = path == Path::kParallel ? pl.doc.n_splits : pl.batched_splits;
   const pp::Workspace ws = pp::carve_workspace(workspace, n_splits, P, H);
 
-  hipError_t e = pp::launch_plan_doclen(sid, seq_len, ws.doc_len, stream);
+  // optional profiling events around the launches
+  auto mark = [&](int i) -> hipError_t {
+    return events ? hipEventRecord(static_cast<hipEvent_t>(events[i]), stream) : hipSuccess;
+  };
+  hipError_t e = mark(0);
+  if (e == hipSuccess) e = pp::launch_plan_doclen(sid, seq_len, ws.plan_parts, stream);
+  if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess) {
-    e = path == Path::kParallel ? pp::launch_doc(pl.doc, q, k, v, P, H, d, dtype, c, ws, stream)
-                                : pp::launch_batched_doc(n_splits, q, k, v, P, H, d, dtype, c, ws, stream);
+    e = path == Path::kParallel ? pp::launch_doc(pl.doc, q, k, v, seq_len, P, H, d, dtype, c, ws, stream)
+                                : pp::launch_batched_doc(n_splits, q, k, v, seq_len, P, H, d, dtype, c, ws, stream);
   }
+  if (e == hipSuccess) e = mark(2);
   if (e == hipSuccess) e = pp::launch_tail_merge(n_splits, q, k, v, sid, seq_len, P, H, d, dtype, c, ws, out, stream);
-  if (e != hipSuccess) return fail(PP_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  if (e == hipSuccess) e = mark(3);
+  if (e != hipSuccess) return fail(PP_ERR_HIP, "kernel launch or event record failed: %s", hipGetErrorString(e));
   return ok();
 }
 
@@ -166,8 +174,22 @@ pp_status_t pp_attn_decode_batched(const void* q, const void* k_cache, const voi
                      workspace_bytes, hip_stream);
 }
 
+pp_status_t pp_attn_decode_profiled(int32_t batched, const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* stream_id, int64_t seq_len, int32_t P, int32_t H, int32_t d,
+                                    float scale, void* out, pp_dtype_t dtype, void* workspace,
+                                    size_t workspace_bytes, void* hip_stream, void* const* events,
+                                    int32_t n_events) {
+  if (!events || n_events < PP_PROFILE_EVENTS)
+    return fail(PP_ERR_INVALID_ARG, "need %d events, got %d", PP_PROFILE_EVENTS, events ? n_events : 0);
+  for (int i = 0; i < PP_PROFILE_EVENTS; ++i)
+    if (!events[i]) return fail(PP_ERR_INVALID_ARG, "events[%d] is null", i);
+  return decode_impl(batched ? Path::kBatched : Path::kParallel, q, k_cache, v_cache, stream_id, seq_len, P, H, d,
+                     scale, out, dtype, workspace, workspace_bytes, hip_stream, events);
+}
+
 pp_status_t pp_attn_plan(const int32_t* stream_id, int64_t seq_len, int32_t P, int32_t* doc_len_out,
-                         int32_t* tail_count_out, int32_t* tail_slots_out, int64_t tail_capacity, void* hip_stream) {
+                         int32_t* tail_count_out, int32_t* tail_slots_out, int64_t tail_capacity, void* workspace,
+                         size_t workspace_bytes, void* hip_stream) {
   if (seq_len < 1 || seq_len > PP_MAX_SEQ_LEN)
     return fail(PP_ERR_INVALID_ARG, "seq_len=%lld out of range", (long long)seq_len);
   if (P < 1 || P > PP_MAX_STREAMS) return fail(PP_ERR_INVALID_ARG, "P=%d out of range", P);
@@ -175,10 +197,14 @@ pp_status_t pp_attn_plan(const int32_t* stream_id, int64_t seq_len, int32_t P, i
   if (tail_capacity < 0 || (tail_capacity > 0 && !tail_slots_out))
     return fail(PP_ERR_INVALID_ARG, "tail_slots_out is null or tail_capacity negative");
   if (!aligned16(stream_id)) return fail(PP_ERR_INVALID_ARG, "stream_id must be 16-byte aligned");
+  if (!workspace || workspace_bytes < PP_PLAN_WORKSPACE_BYTES)
+    return fail(PP_ERR_WORKSPACE, "pp_attn_plan needs %d bytes of workspace", (int)PP_PLAN_WORKSPACE_BYTES);
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-  hipError_t e = pp::launch_plan_doclen(stream_id, seq_len, doc_len_out, stream);
+  const pp::Workspace ws = pp::carve_workspace(workspace, 0, P, 1);
+  hipError_t e = pp::launch_plan_doclen(stream_id, seq_len, ws.plan_parts, stream);
   if (e == hipSuccess)
-    e = pp::launch_plan_lists(stream_id, seq_len, P, doc_len_out, tail_count_out, tail_slots_out, tail_capacity, stream);
+    e = pp::launch_plan_lists(stream_id, seq_len, P, ws.plan_parts, doc_len_out, tail_count_out, tail_slots_out,
+                              tail_capacity, stream);
   if (e != hipSuccess) return fail(PP_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }

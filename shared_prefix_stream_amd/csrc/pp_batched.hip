@@ -45,8 +45,8 @@ __device__ __forceinline__ void to_f32b<float>(const u32x4& w, float* f) {
 template <int VEC>
 __device__ __forceinline__ void merge_b(float& M, float& Ls, float* A, float m2, float l2, const float* A2) {
   const float Mn = fmaxf(M, m2);
-  if (Mn == -INFINITY) return;
-  const float a = fast_exp2(M - Mn), b = fast_exp2(m2 - Mn);
+  const float ref = Mn == -INFINITY ? 0.f : Mn;  // both empty: weights exp2(-inf) = 0
+  const float a = fast_exp2(M - ref), b = fast_exp2(m2 - ref);
   Ls = Ls * a + l2 * b;
 #pragma unroll
   for (int e = 0; e < VEC; ++e) A[e] = A[e] * a + A2[e] * b;
@@ -56,7 +56,7 @@ __device__ __forceinline__ void merge_b(float& M, float& Ls, float* A, float m2,
 template <typename T, int D>
 __global__ __launch_bounds__(kBThreads) void batched_doc_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, int P, int H, float c,
-    const int32_t* __restrict__ doc_len_ptr, int n_splits, float* __restrict__ part_o,
+    const int32_t* __restrict__ plan_parts, int64_t seq_len, int n_splits, float* __restrict__ part_o,
     float2* __restrict__ part_ml) {
   constexpr int VEC = 16 / (int)sizeof(T);
   constexpr int LPK = D / VEC;   // lanes per slot
@@ -67,7 +67,7 @@ __global__ __launch_bounds__(kBThreads) void batched_doc_kernel(
   const int h = blockIdx.x, split = blockIdx.y, s = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int kg = lane / LPK, dl = lane % LPK;
-  const int64_t L = *doc_len_ptr;
+  const int64_t L = doc_prefix_from_parts(plan_parts, seq_len);
   const int64_t j_begin = split * L / n_splits, j_end = (split + 1) * L / n_splits;
   const int64_t row = (int64_t)H * D;
 
@@ -81,15 +81,12 @@ __global__ __launch_bounds__(kBThreads) void batched_doc_kernel(
     u32x4 kr[kBU], vr[kBU];
 #pragma unroll
     for (int u = 0; u < kBU; ++u) {
-      const int64_t j = blk + (int64_t)(wave * kBU + u) * KPI + kg;
-      if (j < j_end) {
-        const int64_t off = j * row + (int64_t)h * D + dl * VEC;
-        kr[u] = *reinterpret_cast<const u32x4*>(k + off);
-        vr[u] = *reinterpret_cast<const u32x4*>(v + off);
-      } else {
-        kr[u] = u32x4{0u, 0u, 0u, 0u};
-        vr[u] = u32x4{0u, 0u, 0u, 0u};
-      }
+      // unconditional load (slots past the split's end re-read its last slot
+      // and are skipped below), so all of them are in flight together
+      const int64_t j = min(blk + (int64_t)(wave * kBU + u) * KPI + kg, j_end - 1);
+      const int64_t off = j * row + (int64_t)h * D + dl * VEC;
+      kr[u] = *reinterpret_cast<const u32x4*>(k + off);
+      vr[u] = *reinterpret_cast<const u32x4*>(v + off);
     }
 #pragma unroll
     for (int u = 0; u < kBU; ++u) {
@@ -168,13 +165,13 @@ int choose_batched_splits(int64_t seq_len, int P, int H, int num_cus) {
   return (int)want;
 }
 
-hipError_t launch_batched_doc(int n_splits, const void* q, const void* k, const void* v, int P, int H, int d,
-                              pp_dtype_t dtype, float c, const Workspace& ws, hipStream_t stream) {
+hipError_t launch_batched_doc(int n_splits, const void* q, const void* k, const void* v, int64_t seq_len, int P,
+                              int H, int d, pp_dtype_t dtype, float c, const Workspace& ws, hipStream_t stream) {
   const dim3 grid(H, n_splits, P);  // dispatch order: heads, then splits, stream outermost
 #define PP_B_LAUNCH(TT, DD)                                                                                   \
   batched_doc_kernel<TT, DD><<<grid, kBThreads, 0, stream>>>(static_cast<const TT*>(q), static_cast<const TT*>(k), \
-                                                             static_cast<const TT*>(v), P, H, c, ws.doc_len,       \
-                                                             n_splits, ws.part_o, ws.part_ml)
+                                                             static_cast<const TT*>(v), P, H, c, ws.plan_parts,    \
+                                                             seq_len, n_splits, ws.part_o, ws.part_ml)
   if (dtype == PP_BF16) {
     if (d == 128) PP_B_LAUNCH(uint16_t, 128);
     else PP_B_LAUNCH(uint16_t, 64);

@@ -24,28 +24,64 @@
 namespace pp {
 namespace {
 
-constexpr int kDocThreads = 256;  // 4 waves; wave w owns queries [w*16*QB, (w+1)*16*QB)
+constexpr int kDocThreads = 256;  // workgroup of the fp32 vector-ALU kernel
 
-// Document slots per tile: 64, or 32 for the widest query tile at d = 128,
-// whose accumulators (64 queries x 128 dims per wave) leave room for no more.
-template <int D, int QB>
-constexpr int doc_tile_keys() { return (D == 128 && QB == 4) ? 32 : 64; }
+// Lazy rescaling threshold (log2 units): the running maximum used as the
+// softmax reference is only raised when a tile's maximum exceeds it by more
+// than this, so exp2(x - m) <= 2^kLazyTau and the O accumulators are rescaled
+// on few tiles.  The final merge uses the same (m, l, O), so the result is
+// unchanged up to rounding.
+constexpr float kLazyTau = 8.0f;
+
+// One direct global->LDS load of 16 bytes per lane (gfx950
+// global_load_lds_dwordx4): lane l's chunk lands at LDS byte lds_base + 16*l.
+// Issued from asm so that the compiler, which cannot tell these LDS writes
+// from the transposing LDS reads below, does not drain every outstanding load
+// before each such read; the kernel waits on its own loads with explicit
+// vmcnt waits instead.  The asm has no outputs, and it sets M0, which the
+// compiler reserves and does not rely on in this kernel.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(const void* gaddr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(gaddr) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+template <int D, int QB, int NW>
+struct DocTile {
+  // Document slots per tile: 64, or 32 for the widest per-wave query tile at
+  // d = 128, whose accumulators (64 queries x 128 dims per wave) leave the
+  // fewest registers.
+  static constexpr int NK = (D == 128 && QB == 4) ? 32 : 64;
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int ROWB = D * 2;                 // bytes of one K or V row (one head)
+  static constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  static constexpr int TILE_BYTES = NK * ROWB;       // K (or V) tile
+  static constexpr int STAGE_BYTES = 2 * TILE_BYTES;
+  static constexpr int NS = STAGE_BYTES <= 16384 ? 4 : 3;  // pipeline depth (stages in LDS)
+  static constexpr int ROWS_PER_KB = 1024 / ROWB;    // rows one wave-wide 16-byte load fills
+  static constexpr int NLD = TILE_BYTES / 1024 / NW;  // direct loads per thread per tile (K or V)
+  static_assert(NLD >= 1 && TILE_BYTES % (1024 * NW) == 0, "tile shape");
+};
 
 // ---- LDS layouts -----------------------------------------------------------
-// K tile: [NK keys][D dims] bf16, 16-byte chunks XOR-swizzled per row so
-// that the 16 rows read by one MFMA A-operand load fall in distinct banks.
-// V tile: stored transposed, [D dims][NK keys] bf16 (rows of 2*NK bytes), so a
-// lane can read the 8 consecutive keys of one dim that the P.V MFMA needs
-// as its A operand; 16-byte granules XOR-swizzled per row.
+// Tiles are filled by direct global->LDS loads: a wave-wide 16-byte load
+// writes 1 KB of LDS contiguously (lane l at +16*l), and each lane may fetch
+// any 16-byte chunk of the tile, so the layouts below are permutations of
+// 16-byte chunks within each row (XOR swizzles that keep MFMA operand reads
+// free of bank conflicts).
+//
+// K tile [NK][D]: the QK A operand of key block kb is read by lane (r, g) as
+// 16 bytes of row key_of(kb, r); those 16 rows differ in key bits 0,1,3,4.
 
 // 4-bit row pattern f(r) with: f bijective on even r, on odd r, on r<8 and
-// on r>=8 (r = 0..15).  Used for 128-byte rows where two rows share one
-// 256-byte bank line.
+// on r>=8 (r = 0..15), for 128-byte rows where two rows share a bank line.
 __device__ __forceinline__ int swz_rows128(int r) { return ((r >> 1) & 3) | (((r & 1) ^ ((r >> 3) & 1)) << 2); }
 
-// K-row swizzle.  The 16 keys of one QK MFMA A operand are
-// {32c + 8(r>>2) + 4b + (r&3)} (r = 0..15), i.e. they differ in key bits
-// 0,1,3,4; the swizzle maps those bits to distinct granules.
 template <int D>
 __device__ __forceinline__ int swz_k(int key) {
   const int r = (key & 3) | (((key >> 3) & 3) << 2);
@@ -56,13 +92,18 @@ __device__ __forceinline__ int swz_k(int key) {
   }
 }
 
-// V^T-row swizzle (16-byte granule index within a row of NK keys).
-template <int NK>
-__device__ __forceinline__ int swz_vt(int row) {
-  if constexpr (NK == 64) {
-    return swz_rows128(row & 15);  // 8 granules per 128-byte row
+// V tile [NK][D], natural row order.  The P.V A operand (8 consecutive keys
+// of one dim per lane) is read with the gfx950 transposing LDS load
+// ds_read_b64_tr_b16: in each 16-lane group, lane 4r+j points at 4
+// consecutive dims of row r, and lane m receives dim m of the 4 rows.  One
+// such load touches rows 8g + r (g = lane/16, r = 0..3) in 32-byte pieces;
+// the swizzle (even, so chunk pairs stay together) spreads them over banks.
+template <int D>
+__device__ __forceinline__ int swz_v(int key) {
+  if constexpr (D == 128) {
+    return 2 * ((key & 3) | (((key >> 3) & 1) << 2));
   } else {
-    return ((row >> 2) & 3) ^ (row & 2);  // 4 granules per 64-byte row
+    return 2 * (((key >> 1) & 1) | (((key >> 3) & 1) << 1));
   }
 }
 
@@ -72,36 +113,46 @@ __device__ __forceinline__ int swz_vt(int row) {
 // supplies as the P.V MFMA operand (g = lane / 16).
 __device__ __forceinline__ int key_of(int kb, int r) { return 32 * (kb >> 1) + 8 * (r >> 2) + 4 * (kb & 1) + (r & 3); }
 
-template <int D, int QB>
-__global__ __launch_bounds__(kDocThreads) void doc_mfma_bf16_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int P,
-    int H, float c, const int32_t* __restrict__ doc_len_ptr, int n_splits, float* __restrict__ part_o,
-    float2* __restrict__ part_ml) {
-  constexpr int kNK = doc_tile_keys<D, QB>();
-  constexpr int KC = D / 32;            // QK contraction steps (32 dims each)
-  constexpr int DB = D / 16;            // 16-dim output blocks
-  constexpr int KB = kNK / 16;          // 16-key blocks per tile
-  constexpr int CH = kNK / 32;          // P.V contraction steps (32 keys each)
-  constexpr int ROWB = D * 2;           // bytes per K row in LDS
-  constexpr int VTB = kNK * 2;          // bytes per V^T row in LDS
-  constexpr int CPR = D / 8;            // 16-byte chunks per K/V row
-  constexpr int NLD = kNK * CPR / kDocThreads;  // 16-byte loads per thread per tile (K and V each)
-  constexpr int KPT = NLD;              // V keys per thread (same dim chunk)
-  static_assert(NLD == 2 || NLD == 4, "tile shape");
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
 
-  __shared__ __attribute__((aligned(16))) unsigned char lds_k[2][kNK * ROWB];
-  __shared__ __attribute__((aligned(16))) unsigned char lds_v[2][D * VTB];
+// Workgroup = NW waves; wave w owns queries [w*16*QB, (w+1)*16*QB) of the
+// workgroup's query tile (16*QB*NW queries).  With 8 waves of 32 queries
+// two waves share each SIMD, so one wave's softmax overlaps the other's
+// matrix products.
+template <int D, int QB, int NW>
+__global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int P,
+    int H, float c, const int32_t* __restrict__ plan_parts, int64_t seq_len, int n_splits,
+    float* __restrict__ part_o, float2* __restrict__ part_ml) {
+  using TL = DocTile<D, QB, NW>;
+  constexpr int NK = TL::NK, NS = TL::NS, NLD = TL::NLD, ROWB = TL::ROWB, CPR = TL::CPR;
+  constexpr int KC = D / 32;   // QK contraction steps (32 dims each)
+  constexpr int DB = D / 16;   // 16-dim output blocks
+  constexpr int KB = NK / 16;  // 16-key blocks per tile
+  constexpr int CH = NK / 32;  // P.V contraction steps (32 keys each)
+
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[NS][TL::STAGE_BYTES];
 
   const int split = blockIdx.x, h = blockIdx.y, pt = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int ln = lane & 15, lg = lane >> 4;
-  const int L = *doc_len_ptr;
-  const int n_tiles = (L + kNK - 1) / kNK;
+  const int L = doc_prefix_from_parts(plan_parts, seq_len);
+  const int n_tiles = (L + NK - 1) / NK;
   const int t0 = (int)((int64_t)split * n_tiles / n_splits);
   const int t1 = (int)((int64_t)(split + 1) * n_tiles / n_splits);
-  const int key_end = min(t1 * kNK, L);
-  const int q0 = pt * (64 * QB) + wave * (16 * QB);
+  const int key_end = min(t1 * NK, L);
+  const int q0 = pt * (16 * QB * NW) + wave * (16 * QB);
   const int64_t row = (int64_t)H * D;  // elements between consecutive slots
+
+  // Scores are taken as x = s * |c| with the sign of c folded into Q (a bf16
+  // sign flip is exact), so the running maximum of x is that of s.
+  const uint32_t qsign = c < 0.f ? 0x80008000u : 0u;
+  const float cabs = fabsf(c);
 
   // Q fragments (B operand of S^T = K Q^T): lane (query ln, group lg) holds
   // dims kc*32 + 8*lg .. +8 of its query.  Padding queries are zero.
@@ -111,11 +162,10 @@ __global__ __launch_bounds__(kDocThreads) void doc_mfma_bf16_kernel(
     const int p = q0 + qb * 16 + ln;
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
-      if (p < P) {
-        qf[qb][kc] = *reinterpret_cast<const bf16x8*>(q + ((int64_t)p * H + h) * D + kc * 32 + lg * 8);
-      } else {
-        qf[qb][kc] = bf16x8{};
-      }
+      u32x4 w = u32x4{0u, 0u, 0u, 0u};
+      if (p < P) w = *reinterpret_cast<const u32x4*>(q + ((int64_t)p * H + h) * D + kc * 32 + lg * 8);
+      w ^= qsign;
+      qf[qb][kc] = __builtin_bit_cast(bf16x8, w);
     }
   }
 
@@ -129,159 +179,155 @@ __global__ __launch_bounds__(kDocThreads) void doc_mfma_bf16_kernel(
     for (int db = 0; db < DB; ++db) o[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  if (t0 < t1) {
-    u32x4 kreg[NLD], vreg[NLD];
-
-    // global -> registers for tile t (coalesced 16-byte loads; rows past
-    // key_end are zero and never read from memory)
-    auto gload = [&](int t) {
-      const int kbase = t * kNK;
+  // Direct global->LDS loads of tile t into stage st.  Wave w's i-th load
+  // fills 1 KB block (i*NW + w) of the K and of the V tile; rows past the
+  // split's end re-read its last row (finite data, masked out of the scores).
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t ring_base = lds_addr(&ring[0][0]);
+  auto issue = [&](int t, int st) {
+    const uint32_t ks = ring_base + st * TL::STAGE_BYTES;
+    const uint32_t vs = ks + TL::TILE_BYTES;
+    const int kbase = t * NK;
 #pragma unroll
-      for (int i = 0; i < NLD; ++i) {
-        const int cidx = tid + i * kDocThreads;
-        const int key = cidx / CPR, col = cidx % CPR;
-        const int gk = kbase + key;
-        kreg[i] = gk < key_end ? *reinterpret_cast<const u32x4*>(k + (int64_t)gk * row + (int64_t)h * D + col * 8)
-                               : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < NLD; ++i) {
+      const int blk = i * NW + wave_u;
+      const int r = blk * TL::ROWS_PER_KB + lane / CPR;
+      const int slot = lane % CPR;
+      const int64_t g = (int64_t)min(kbase + r, key_end - 1) * row + (int64_t)h * D;
+      lds_dma16(k + g + (slot ^ swz_k<D>(r)) * 8, ks + blk * 1024);
+      lds_dma16(v + g + (slot ^ swz_v<D>(r)) * 8, vs + blk * 1024);
+    }
+  };
+
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (t0 + s < t1) issue(t0 + s, s);
+
+  for (int t = t0; t < t1; ++t) {
+    const int st = (t - t0) % NS;
+    // tile t's loads are complete once at most the younger tiles' remain
+    const int younger = min(NS - 2, t1 - 1 - t);
+    if (younger >= 2) wait_vmcnt<2 * 2 * NLD>();
+    else if (younger == 1) wait_vmcnt<2 * NLD>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();        // every wave's loads of tile t are in LDS, and
+    asm volatile("" ::: "memory");       // every wave is done reading stage (t-1) % NS
+    if (t + NS - 1 < t1) issue(t + NS - 1, (t - t0 + NS - 1) % NS);
+
+    const unsigned char* ks = ring[st];
+    const unsigned char* vs = ring[st] + TL::TILE_BYTES;
+    const int kbase = t * NK;
+
+    // ---- S^T = K Q^T -------------------------------------------------------
+    f32x4 s[QB][KB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) s[qb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int key = key_of(kb, ln);
+        const int col = kc * 4 + lg;
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + key * ROWB + ((col ^ swz_k<D>(key)) * 16));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          s[qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[qb][kc], s[qb][kb], 0, 0, 0);
       }
-      const int dc = tid % CPR, kq = tid / CPR;
-#pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        const int gk = kbase + kq * KPT + i;
-        vreg[i] = gk < key_end ? *reinterpret_cast<const u32x4*>(v + (int64_t)gk * row + (int64_t)h * D + dc * 8)
-                               : u32x4{0u, 0u, 0u, 0u};
-      }
-    };
+    }
 
-    // registers -> LDS buffer b (K swizzled, V transposed + swizzled)
-    auto lstore = [&](int b) {
-#pragma unroll
-      for (int i = 0; i < NLD; ++i) {
-        const int cidx = tid + i * kDocThreads;
-        const int key = cidx / CPR, col = cidx % CPR;
-        *reinterpret_cast<u32x4*>(&lds_k[b][key * ROWB + ((col ^ swz_k<D>(key)) * 16)]) = kreg[i];
-      }
-      const int dc = tid % CPR, kq = tid / CPR;
-      // vreg[i] holds dims dc*8 .. +8 of key kq*KPT + i; dword w = dims 2w (lo), 2w+1 (hi)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int dim = dc * 8 + 2 * w + half;
-          uint32_t pk[KPT / 2];
-#pragma unroll
-          for (int j = 0; j < KPT / 2; ++j) {
-            const uint32_t a = vreg[2 * j][w], bb = vreg[2 * j + 1][w];
-            pk[j] = half == 0 ? ((a & 0xffffu) | (bb << 16)) : ((a >> 16) | (bb & 0xffff0000u));
-          }
-          const int key0 = kq * KPT;              // first key written
-          const int gi = key0 / 8;                // 16-byte granule within the row
-          const int off = (key0 % 8) * 2;         // byte offset within the granule
-          unsigned char* dst = &lds_v[b][dim * VTB + ((gi ^ swz_vt<kNK>(dim)) * 16) + off];
-          if constexpr (KPT == 4) {
-            *reinterpret_cast<uint2*>(dst) = make_uint2(pk[0], pk[1]);
-          } else {
-            *reinterpret_cast<uint32_t*>(dst) = pk[0];
-          }
-        }
-      }
-    };
-
-    gload(t0);
-    lstore(0);
-    __syncthreads();
-
-    for (int t = t0; t < t1; ++t) {
-      const int b = (t - t0) & 1;
-      if (t + 1 < t1) gload(t + 1);
-      const int kbase = t * kNK;
-
-      // ---- S^T = K Q^T -----------------------------------------------------
-      f32x4 s[QB][KB];
+    // ---- online softmax, base 2, lazy rescale ------------------------------
+    if (kbase + NK > key_end) {  // ragged last tile of the split (uniform)
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) s[qb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const int key = key_of(kb, ln);
-          const int col = kc * 4 + lg;
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&lds_k[b][key * ROWB + ((col ^ swz_k<D>(key)) * 16)]);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            s[qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[qb][kc], s[qb][kb], 0, 0, 0);
-        }
-      }
-
-      // ---- online softmax (log2 domain); lane holds keys of its group lg ----
-      uint32_t pb[QB][CH][4];  // P^T as packed bf16 pairs: the P.V B operand
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        float tmax = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int key = 32 * (kb >> 1) + 8 * lg + 4 * (kb & 1) + i;
-            const float x = (kbase + key < key_end) ? s[qb][kb][i] * c : -INFINITY;
-            s[qb][kb][i] = x;
-            tmax = fmaxf(tmax, x);
+            if (kbase + key >= key_end) s[qb][kb][i] = -INFINITY;
           }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float mn = fmaxf(m[qb], tmax);  // finite: every tile has a valid key
+    }
+    // running maxima: lane (query ln, group lg) holds 4*KB keys of its query;
+    // reduce over the 4 groups with lane swaps
+    float tmax[QB];
+    bool grow = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float smax = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) smax = fmaxf(smax, s[qb][kb][i]);
+      smax = max_xor32(max_xor16(smax));
+      tmax[qb] = smax * cabs;
+      grow |= tmax[qb] > m[qb] + kLazyTau;
+    }
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform, rare after the first tile
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float mn = fmaxf(m[qb], tmax[qb]);
         const float alpha = fast_exp2(m[qb] - mn);
         m[qb] = mn;
-        float psum = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float p = fast_exp2(s[qb][kb][i] - mn);
-            s[qb][kb][i] = p;
-            psum += p;
-          }
-        l[qb] = l[qb] * alpha + psum;
+        l[qb] *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db) o[qb][db] *= alpha;
-#pragma unroll
-        for (int ch = 0; ch < CH; ++ch) {
-          pb[qb][ch][0] = pack_bf16x2(s[qb][2 * ch][0], s[qb][2 * ch][1]);
-          pb[qb][ch][1] = pack_bf16x2(s[qb][2 * ch][2], s[qb][2 * ch][3]);
-          pb[qb][ch][2] = pack_bf16x2(s[qb][2 * ch + 1][0], s[qb][2 * ch + 1][1]);
-          pb[qb][ch][3] = pack_bf16x2(s[qb][2 * ch + 1][2], s[qb][2 * ch + 1][3]);
-        }
       }
-
-      // ---- O^T += V^T P^T ----------------------------------------------------
+    }
+    uint32_t pb[QB][CH][4];  // P^T as packed bf16 pairs: the P.V B operand
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float mneg = -m[qb];
+      float psum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = fast_exp2(fmaf(s[qb][kb][i], cabs, mneg));
+          s[qb][kb][i] = p;
+          psum += p;
+        }
+      l[qb] += psum;
 #pragma unroll
       for (int ch = 0; ch < CH; ++ch) {
+        pb[qb][ch][0] = pack_bf16x2(s[qb][2 * ch][0], s[qb][2 * ch][1]);
+        pb[qb][ch][1] = pack_bf16x2(s[qb][2 * ch][2], s[qb][2 * ch][3]);
+        pb[qb][ch][2] = pack_bf16x2(s[qb][2 * ch + 1][0], s[qb][2 * ch + 1][1]);
+        pb[qb][ch][3] = pack_bf16x2(s[qb][2 * ch + 1][2], s[qb][2 * ch + 1][3]);
+      }
+    }
+
+    // ---- O^T += V^T P^T ----------------------------------------------------
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int dim = db * 16 + ln;
-          const int gi = ch * 4 + lg;
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&lds_v[b][dim * VTB + ((gi ^ swz_vt<kNK>(dim)) * 16)]);
+    for (int ch = 0; ch < CH; ++ch) {
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) {
-            const u32x4 bw = u32x4{pb[qb][ch][0], pb[qb][ch][1], pb[qb][ch][2], pb[qb][ch][3]};
-            o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, bw), o[qb][db], 0, 0, 0);
-          }
+      for (int db = 0; db < DB; ++db) {
+        // lane (ln, lg) points at row 32ch + 8lg + 4half + ln/4, dims db*16 + 4(ln%4) .. +4
+        bf16x4 half2[2];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int key = 32 * ch + 8 * lg + 4 * half + (ln >> 2);
+          const int dim = db * 16 + 4 * (ln & 3);
+          const int chunk = dim >> 3;
+          const unsigned char* src = vs + key * ROWB + ((chunk ^ swz_v<D>(key)) * 16) + (dim & 7) * 2;
+          half2[half] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (__attribute__((address_space(3))) bf16x4*)(src));
+        }
+        const bf16x8 a = __builtin_shufflevector(half2[0], half2[1], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const u32x4 bw = u32x4{pb[qb][ch][0], pb[qb][ch][1], pb[qb][ch][2], pb[qb][ch][3]};
+          o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, bw), o[qb][db], 0, 0, 0);
         }
       }
-
-      if (t + 1 < t1) lstore(b ^ 1);
-      __syncthreads();
     }
   }
 
   // ---- partial state of this split -------------------------------------------
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    float lt = l[qb];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
+    const float lt = sum_xor32(sum_xor16(l[qb]));
     const int p = q0 + qb * 16 + ln;
     if (p < P) {
       const int64_t sh = ((int64_t)split * P + p) * H + h;
@@ -302,13 +348,14 @@ constexpr int kF32NK = 32;
 template <int D>
 __global__ __launch_bounds__(kDocThreads) void doc_valu_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v, int P, int H, float c,
-    const int32_t* __restrict__ doc_len_ptr, int n_splits, float* __restrict__ part_o, float2* __restrict__ part_ml) {
+    const int32_t* __restrict__ plan_parts, int64_t seq_len, int n_splits, float* __restrict__ part_o,
+    float2* __restrict__ part_ml) {
   __shared__ __attribute__((aligned(16))) float lk[kF32NK][D];
   __shared__ __attribute__((aligned(16))) float lv[kF32NK][D];
   const int split = blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x;
   const int p = blockIdx.z * kDocThreads + tid;
-  const int L = *doc_len_ptr;
+  const int L = doc_prefix_from_parts(plan_parts, seq_len);
   const int n_tiles = (L + kF32NK - 1) / kF32NK;
   const int t0 = (int)((int64_t)split * n_tiles / n_splits);
   const int t1 = (int)((int64_t)(split + 1) * n_tiles / n_splits);
@@ -377,11 +424,16 @@ DocPlan choose_doc_plan(int64_t seq_len, int P, int H, int d, pp_dtype_t dtype, 
   DocPlan pl;
   int per_cu;  // workgroups resident per CU the launch is sized for
   if (dtype == PP_BF16) {
-    pl.qb = P <= 64 ? 1 : (P <= 128 ? 2 : 4);
-    pl.n_ptiles = (P + 64 * pl.qb - 1) / (64 * pl.qb);
-    per_cu = pl.qb == 4 ? 1 : 2;
+    // 16-query blocks per wave and waves per workgroup: (1, 4) for P <= 64,
+    // (2, 4) for P <= 128, else (2, 8): 256 queries of a head per workgroup
+    pl.qb = P <= 64 ? 1 : 2;
+    pl.nw = P <= 128 ? 4 : 8;
+    const int per_wg = 16 * pl.qb * pl.nw;
+    pl.n_ptiles = (P + per_wg - 1) / per_wg;
+    per_cu = 1;
   } else {
     pl.qb = 0;
+    pl.nw = 4;
     pl.n_ptiles = (P + kDocThreads - 1) / kDocThreads;
     per_cu = 2;
   }
@@ -395,23 +447,24 @@ DocPlan choose_doc_plan(int64_t seq_len, int P, int H, int d, pp_dtype_t dtype, 
   return pl;
 }
 
-hipError_t launch_doc(const DocPlan& pl, const void* q, const void* k, const void* v, int P, int H, int d,
-                      pp_dtype_t dtype, float c, const Workspace& ws, hipStream_t stream) {
+hipError_t launch_doc(const DocPlan& pl, const void* q, const void* k, const void* v, int64_t seq_len, int P, int H,
+                      int d, pp_dtype_t dtype, float c, const Workspace& ws, hipStream_t stream) {
   const dim3 grid(pl.n_splits, H, pl.n_ptiles);
   if (dtype == PP_BF16) {
     auto* qq = static_cast<const uint16_t*>(q);
     auto* kk = static_cast<const uint16_t*>(k);
     auto* vv = static_cast<const uint16_t*>(v);
-#define PP_DOC_LAUNCH(DD, QQ) \
-  doc_mfma_bf16_kernel<DD, QQ><<<grid, kDocThreads, 0, stream>>>(qq, kk, vv, P, H, c, ws.doc_len, pl.n_splits, ws.part_o, ws.part_ml)
+#define PP_DOC_LAUNCH(DD, QQ, WW)                                                                      \
+  doc_mfma_bf16_kernel<DD, QQ, WW><<<grid, 64 * WW, 0, stream>>>(qq, kk, vv, P, H, c, ws.plan_parts, \
+                                                                  seq_len, pl.n_splits, ws.part_o, ws.part_ml)
     if (d == 128) {
-      if (pl.qb == 1) PP_DOC_LAUNCH(128, 1);
-      else if (pl.qb == 2) PP_DOC_LAUNCH(128, 2);
-      else PP_DOC_LAUNCH(128, 4);
+      if (pl.qb == 1) PP_DOC_LAUNCH(128, 1, 4);
+      else if (pl.nw == 4) PP_DOC_LAUNCH(128, 2, 4);
+      else PP_DOC_LAUNCH(128, 2, 8);
     } else {
-      if (pl.qb == 1) PP_DOC_LAUNCH(64, 1);
-      else if (pl.qb == 2) PP_DOC_LAUNCH(64, 2);
-      else PP_DOC_LAUNCH(64, 4);
+      if (pl.qb == 1) PP_DOC_LAUNCH(64, 1, 4);
+      else if (pl.nw == 4) PP_DOC_LAUNCH(64, 2, 4);
+      else PP_DOC_LAUNCH(64, 2, 8);
     }
 #undef PP_DOC_LAUNCH
   } else {
@@ -419,9 +472,9 @@ hipError_t launch_doc(const DocPlan& pl, const void* q, const void* k, const voi
     auto* kk = static_cast<const float*>(k);
     auto* vv = static_cast<const float*>(v);
     if (d == 128)
-      doc_valu_f32_kernel<128><<<grid, kDocThreads, 0, stream>>>(qq, kk, vv, P, H, c, ws.doc_len, pl.n_splits, ws.part_o, ws.part_ml);
+      doc_valu_f32_kernel<128><<<grid, kDocThreads, 0, stream>>>(qq, kk, vv, P, H, c, ws.plan_parts, seq_len, pl.n_splits, ws.part_o, ws.part_ml);
     else
-      doc_valu_f32_kernel<64><<<grid, kDocThreads, 0, stream>>>(qq, kk, vv, P, H, c, ws.doc_len, pl.n_splits, ws.part_o, ws.part_ml);
+      doc_valu_f32_kernel<64><<<grid, kDocThreads, 0, stream>>>(qq, kk, vv, P, H, c, ws.plan_parts, seq_len, pl.n_splits, ws.part_o, ws.part_ml);
   }
   return hipGetLastError();
 }

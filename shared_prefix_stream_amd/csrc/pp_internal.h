@@ -11,17 +11,18 @@ namespace pp {
 
 // ----------------------------------------------------------------- types ---
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
 // Workspace layout (byte offsets from a 256-byte aligned base):
-//   [0, 256)              int32 doc_len (leading run of id-0 slots)
+//   [0, 256)              int32 plan_parts[64]: per-chunk first non-document slot
 //   [256, 256 + ML)       float2 part_ml[n_splits][P][H]  (m in log2 units, l)
 //   [..., + O)            float  part_o [n_splits][P][H][d] (unnormalised)
 struct Workspace {
-  int32_t* doc_len;
+  int32_t* plan_parts;
   float2* part_ml;
   float* part_o;
 };
@@ -37,7 +38,7 @@ inline size_t workspace_bytes_for(int n_splits, int64_t P, int64_t H, int64_t d)
 inline Workspace carve_workspace(void* ws, int n_splits, int64_t P, int64_t H) {
   uintptr_t base = align_up((uintptr_t)ws, 256);
   Workspace w;
-  w.doc_len = reinterpret_cast<int32_t*>(base);
+  w.plan_parts = reinterpret_cast<int32_t*>(base);
   w.part_ml = reinterpret_cast<float2*>(base + 256);
   size_t ml = align_up((size_t)n_splits * P * H * sizeof(float2), 256);
   w.part_o = reinterpret_cast<float*>(base + 256 + ml);
@@ -71,6 +72,42 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
+// Reductions across the four 16-lane rows of a wave with the gfx950 VALU
+// lane swaps (no LDS round trip): permlane16_swap(x, x) returns, on every
+// lane, {x of the even 16-lane row, x of the odd row} of its row pair (lane
+// and lane ^ 16); permlane32_swap likewise {lower half, upper half} for lane
+// and lane ^ 32.  Both lanes of a pair therefore compute the same value.
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// ---------------------------------------------------- document prefix ---
+// The plan kernel writes, for each of kPlanWGs workgroups, the first slot
+// with a non-zero id among the chunks it scanned (INT_MAX if none).  The
+// document prefix length is the minimum of those and seq_len; every wave of
+// a consumer computes it from the 64 partials (one load per lane, L2-hot).
+constexpr int kPlanWGs = 64;
+
+__device__ __forceinline__ int doc_prefix_from_parts(const int32_t* __restrict__ parts, int64_t seq_len) {
+  int x = parts[threadIdx.x & 63];
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) x = min(x, __shfl_xor(x, o));
+  return (int64_t)x < seq_len ? x : (int)seq_len;
+}
+
 // ------------------------------------------------- visibility compaction ---
 // Ascending compaction of the slots j in [from, seq_len) that stream s sees
 // past the document prefix: sid[j] == s1 (= s + 1, its own slots) or
@@ -78,50 +115,49 @@ __device__ __forceinline__ float group_max(float v) {
 // project page, "How it works", item 1: a stream sees the document and its
 // own earlier tokens only.]
 //
-// All NT threads of the workgroup call it together.  Work goes in chunks of
-// kCollectChunk slots; thread t owns the contiguous run of U = chunk / NT
-// slots starting at chunk_base + t*U, read as 16-byte int4 granules (the
-// caller guarantees sid is 16-byte aligned; a granule that straddles
-// seq_len lies in one page with a valid element, and its extra entries are
-// ignored).  Matches are written to list[0..) in slot order using one
-// workgroup-wide exclusive scan per chunk, so the order is deterministic and
-// no atomics are used.  Collection stops before a chunk whose matches would
-// not fit in `cap` (cap >= kCollectChunk), returning the count and the first
-// slot not yet examined in *next.  `scan` is LDS scratch of NT/64 + 1 ints.
-constexpr int kCollectChunk = 4096;
-
-template <int NT>
+// All NT threads of the workgroup call it together.  The scan goes in
+// chunks of NT*U slots; thread t owns the contiguous run of U slots starting
+// at chunk_base + t*U, read as 16-byte int4 granules (the caller guarantees
+// sid is 16-byte aligned; loads are unconditional at clamped granules, and a
+// granule that straddles seq_len lies in one page with a valid element; its
+// extra entries are ignored).  Matches go to list[0..cap) in slot order via
+// one workgroup-wide exclusive scan per chunk: deterministic, no atomics.
+// When more than cap slots match, the first cap are kept and *next is the
+// slot after the last kept one; otherwise *next = seq_len.  `scan` is LDS
+// scratch of NT/64 + 2 ints.
+template <int NT, int U>
 __device__ int collect_visible(const int32_t* __restrict__ sid, int64_t from, int64_t seq_len, int s1,
                                int* list, int cap, int64_t* next, int* scan) {
-  static_assert(NT % 64 == 0 && kCollectChunk % (4 * NT) == 0, "bad workgroup size");
-  constexpr int U = kCollectChunk / NT;  // slots per thread per chunk
-  constexpr int G = U / 4;               // int4 granules per thread
+  static_assert(NT % 64 == 0 && U % 4 == 0 && U <= 64, "bad shape");
+  constexpr int G = U / 4;  // int4 granules per thread
   constexpr int NW = NT / 64;
+  constexpr int64_t CHUNK = (int64_t)NT * U;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int count = 0;
-  int64_t cb = from & ~(int64_t)3;  // granule-aligned chunk base
+  int64_t cb = from & ~(int64_t)3;                        // granule-aligned chunk base
+  const int64_t last_gran = (seq_len - 1) & ~(int64_t)3;  // last granule holding a slot < seq_len
+  int64_t nxt = seq_len;
   while (cb < seq_len) {
+    if (count == cap) {  // full at a chunk boundary: resume at this chunk
+      nxt = cb;
+      break;
+    }
     const int64_t j0 = cb + (int64_t)tid * U;
-    int ids[U];
+    uint64_t match = 0;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      int4 x = make_int4(-1, -1, -1, -1);
-      if (j0 + 4 * g < seq_len) x = *reinterpret_cast<const int4*>(sid + j0 + 4 * g);
-      ids[4 * g + 0] = x.x;
-      ids[4 * g + 1] = x.y;
-      ids[4 * g + 2] = x.z;
-      ids[4 * g + 3] = x.w;
-    }
-    unsigned match = 0;
+      const int64_t jg = j0 + 4 * g;
+      const int4 x = *reinterpret_cast<const int4*>(sid + (jg < last_gran ? jg : last_gran));
+      const int ids[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t j = j0 + u;
-      const bool vis = (j >= from) && (j < seq_len) && (ids[u] == 0 || ids[u] == s1);
-      match |= (vis ? 1u : 0u) << u;
+      for (int e = 0; e < 4; ++e) {
+        const int64_t j = jg + e;
+        const bool vis = (j >= from) && (j < seq_len) && (ids[e] == 0 || ids[e] == s1);
+        match |= (vis ? 1ull : 0ull) << (4 * g + e);
+      }
     }
-    const int c = __popc(match);
-    // workgroup exclusive scan of c
-    int incl = c;
+    const int c = __popcll(match);
+    int incl = c;  // wave-inclusive prefix of c
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const int y = __shfl_up(incl, o);
@@ -140,32 +176,40 @@ __device__ int collect_visible(const int32_t* __restrict__ sid, int64_t from, in
     }
     __syncthreads();
     const int total = scan[NW];
-    if (count + total > cap) {
-      __syncthreads();
-      break;  // uniform: every thread read the same total
-    }
     int pos = count + scan[wave] + incl - c;
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (match & (1u << u)) list[pos++] = (int)(j0 + u);
+    uint64_t mm = match;
+    while (mm) {
+      const int u = __ffsll((long long)mm) - 1;
+      mm &= mm - 1;
+      if (pos < cap) list[pos] = (int)(j0 + u);
+      if (pos == cap - 1) scan[NW + 1] = (int)(j0 + u + 1);  // resume point after the last kept slot
+      ++pos;
+    }
+    __syncthreads();
+    if (count + total > cap) {  // uniform: every thread read the same total
+      count = cap;
+      nxt = scan[NW + 1];
+      break;
+    }
     count += total;
-    cb += kCollectChunk;
+    cb += CHUNK;
     __syncthreads();  // scan[] is reused by the next chunk
   }
-  *next = cb < seq_len ? cb : seq_len;
-  __syncthreads();  // list[] complete for every thread
+  *next = nxt;
+  __syncthreads();  // list[] complete for every thread; scan[] free again
   return count;
 }
 
 // ---------------------------------------------------------- host launchers ---
 // Each returns hipSuccess or the launch error.  All enqueue on `stream`.
 
-// doc_len = leading run of id-0 slots of stream_id[0, seq_len).
-hipError_t launch_plan_doclen(const int32_t* sid, int64_t seq_len, int32_t* doc_len, hipStream_t stream);
+// plan_parts[kPlanWGs]: per-workgroup first non-document slot of stream_id[0, seq_len).
+hipError_t launch_plan_doclen(const int32_t* sid, int64_t seq_len, int32_t* plan_parts, hipStream_t stream);
 
-// Integer plan inspection (pp_attn_plan).
-hipError_t launch_plan_lists(const int32_t* sid, int64_t seq_len, int P, const int32_t* doc_len,
-                             int32_t* counts, int32_t* slots, int64_t cap, hipStream_t stream);
+// Integer plan inspection (pp_attn_plan): doc_len, per-stream visible tail
+// counts and slot lists, from the same device code the attention kernels use.
+hipError_t launch_plan_lists(const int32_t* sid, int64_t seq_len, int P, const int32_t* plan_parts,
+                             int32_t* doc_len, int32_t* counts, int32_t* slots, int64_t cap, hipStream_t stream);
 
 // Document part, all P queries of a head at once: split-K partial softmax
 // states over [0, doc_len).  Returns the number of splits it will use via
@@ -173,17 +217,18 @@ hipError_t launch_plan_lists(const int32_t* sid, int64_t seq_len, int P, const i
 struct DocPlan {
   int n_splits;
   int qb;        // 16-query blocks per wave (bf16 MFMA path)
+  int nw;        // waves per workgroup (bf16 MFMA path)
   int n_ptiles;  // query tiles per head
 };
 DocPlan choose_doc_plan(int64_t seq_len, int P, int H, int d, pp_dtype_t dtype, int num_cus);
-hipError_t launch_doc(const DocPlan& plan, const void* q, const void* k, const void* v, int P, int H,
-                      int d, pp_dtype_t dtype, float scale_log2, const Workspace& ws, hipStream_t stream);
+hipError_t launch_doc(const DocPlan& plan, const void* q, const void* k, const void* v, int64_t seq_len, int P,
+                      int H, int d, pp_dtype_t dtype, float scale_log2, const Workspace& ws, hipStream_t stream);
 
 // Per-question document part (the "batched requests" baseline): every
 // stream reads the document itself.
 int choose_batched_splits(int64_t seq_len, int P, int H, int num_cus);
-hipError_t launch_batched_doc(int n_splits, const void* q, const void* k, const void* v, int P, int H,
-                              int d, pp_dtype_t dtype, float scale_log2, const Workspace& ws,
+hipError_t launch_batched_doc(int n_splits, const void* q, const void* k, const void* v, int64_t seq_len, int P,
+                              int H, int d, pp_dtype_t dtype, float scale_log2, const Workspace& ws,
                               hipStream_t stream);
 
 // Own-slot gather for every stream, then the fixed-order merge of the doc

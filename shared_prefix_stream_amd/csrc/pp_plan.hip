@@ -10,56 +10,65 @@
 namespace pp {
 namespace {
 
-constexpr int kPlanThreads = 1024;
-constexpr int kPlanUnroll = 16;
+constexpr int kPlanThreads = 256;
+constexpr int kPlanIds = 16;                              // ids per thread per chunk (4 int4 loads)
+constexpr int64_t kPlanChunk = (int64_t)kPlanThreads * kPlanIds;
 
-// doc_len = index of the first slot whose id is not 0 (or seq_len).  One
-// workgroup scans in chunks of 16K slots, 16 independent loads per thread
-// in flight, and stops at the first chunk that holds a non-zero id.
+// Workgroup b scans chunks b, b + kPlanWGs, ... in increasing order and
+// records the first slot whose id is not 0; it stops at the first chunk that
+// holds one.  Loads are unconditional (clamped granules), one round trip per
+// chunk.
 __global__ __launch_bounds__(kPlanThreads) void plan_doclen_kernel(const int32_t* __restrict__ sid,
                                                                    int64_t seq_len,
-                                                                   int32_t* __restrict__ doc_len) {
+                                                                   int32_t* __restrict__ parts) {
   __shared__ int found;
   const int tid = threadIdx.x;
   if (tid == 0) found = 0x7fffffff;
   __syncthreads();
-  for (int64_t base = 0; base < seq_len; base += (int64_t)kPlanThreads * kPlanUnroll) {
-    int ids[kPlanUnroll];
-#pragma unroll
-    for (int u = 0; u < kPlanUnroll; ++u) {
-      const int64_t j = base + (int64_t)u * kPlanThreads + tid;
-      ids[u] = j < seq_len ? sid[j] : 0;
-    }
+  const int64_t last_gran = (seq_len - 1) & ~(int64_t)3;
+  for (int64_t cb = (int64_t)blockIdx.x * kPlanChunk; cb < seq_len; cb += kPlanWGs * kPlanChunk) {
+    const int64_t j0 = cb + (int64_t)tid * kPlanIds;
     int first = 0x7fffffff;
 #pragma unroll
-    for (int u = kPlanUnroll - 1; u >= 0; --u)
-      if (ids[u] != 0) first = (int)(base + (int64_t)u * kPlanThreads + tid);
+    for (int g = kPlanIds / 4 - 1; g >= 0; --g) {
+      const int64_t jg = j0 + 4 * g;
+      const int4 x = *reinterpret_cast<const int4*>(sid + (jg < last_gran ? jg : last_gran));
+      const int ids[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int e = 3; e >= 0; --e)
+        if (jg + e < seq_len && ids[e] != 0) first = (int)(jg + e);
+    }
     if (first != 0x7fffffff) atomicMin(&found, first);
     __syncthreads();
     const bool done = found != 0x7fffffff;
-    __syncthreads();  // every thread has read `found` before the next chunk
+    __syncthreads();  // every thread has read `found` before it can change again
     if (done) break;
   }
-  if (tid == 0) *doc_len = found == 0x7fffffff ? (int32_t)seq_len : found;
+  if (tid == 0) parts[blockIdx.x] = found;
 }
 
 constexpr int kListThreads = 256;
+constexpr int kListScanU = 64;
+constexpr int kListCap = 2048;
 
 // One workgroup per stream: the same ascending compaction the tail kernel
 // runs, written out for inspection.
 __global__ __launch_bounds__(kListThreads) void plan_lists_kernel(const int32_t* __restrict__ sid,
                                                                   int64_t seq_len,
-                                                                  const int32_t* __restrict__ doc_len,
+                                                                  const int32_t* __restrict__ parts,
+                                                                  int32_t* __restrict__ doc_len_out,
                                                                   int32_t* __restrict__ counts,
                                                                   int32_t* __restrict__ slots, int64_t cap) {
-  __shared__ int list[kCollectChunk];
-  __shared__ int scan[kListThreads / 64 + 1];
+  __shared__ int list[kListCap];
+  __shared__ int scan[kListThreads / 64 + 2];
   const int s = blockIdx.x;
-  int64_t from = *doc_len;
+  const int doc_len = doc_prefix_from_parts(parts, seq_len);
+  if (s == 0 && threadIdx.x == 0) *doc_len_out = doc_len;
+  int64_t from = doc_len;
   int64_t total = 0;
   while (from < seq_len) {
     int64_t next;
-    const int n = collect_visible<kListThreads>(sid, from, seq_len, s + 1, list, kCollectChunk, &next, scan);
+    const int n = collect_visible<kListThreads, kListScanU>(sid, from, seq_len, s + 1, list, kListCap, &next, scan);
     for (int i = threadIdx.x; i < n; i += kListThreads)
       if (total + i < cap) slots[(int64_t)s * cap + total + i] = list[i];
     total += n;
@@ -71,14 +80,14 @@ __global__ __launch_bounds__(kListThreads) void plan_lists_kernel(const int32_t*
 
 }  // namespace
 
-hipError_t launch_plan_doclen(const int32_t* sid, int64_t seq_len, int32_t* doc_len, hipStream_t stream) {
-  plan_doclen_kernel<<<1, kPlanThreads, 0, stream>>>(sid, seq_len, doc_len);
+hipError_t launch_plan_doclen(const int32_t* sid, int64_t seq_len, int32_t* parts, hipStream_t stream) {
+  plan_doclen_kernel<<<kPlanWGs, kPlanThreads, 0, stream>>>(sid, seq_len, parts);
   return hipGetLastError();
 }
 
-hipError_t launch_plan_lists(const int32_t* sid, int64_t seq_len, int P, const int32_t* doc_len,
+hipError_t launch_plan_lists(const int32_t* sid, int64_t seq_len, int P, const int32_t* parts, int32_t* doc_len,
                              int32_t* counts, int32_t* slots, int64_t cap, hipStream_t stream) {
-  plan_lists_kernel<<<P, kListThreads, 0, stream>>>(sid, seq_len, doc_len, counts, slots, cap);
+  plan_lists_kernel<<<P, kListThreads, 0, stream>>>(sid, seq_len, parts, doc_len, counts, slots, cap);
   return hipGetLastError();
 }
 

@@ -5,20 +5,21 @@
 // Prompting project page, "How it works", item 1).  Instead of testing the
 // stream rule on every slot for every stream -- which makes each stream scan
 // its siblings' answers, the cost the project page's "More results" section
-// blames for the smaller gain on long answers -- each workgroup here
-// compacts the slots its own stream sees (ascending, one workgroup-wide scan
-// per 4096-slot chunk) and gathers only those rows.  A slot's K row over all
-// heads is H*d contiguous elements, so waves read whole 16-byte vectors,
-// coalesced.
+// blames for the smaller gain on long answers -- each workgroup compacts the
+// slots its own stream sees (ascending, one workgroup-wide scan per 16K-slot
+// chunk) and gathers only those rows.
 //
-// Workgroup = one stream x a block of heads.  Wave w handles head group
-// (w % HGW) -- GW consecutive heads, i.e. a contiguous GW*d-element slice of
-// each K/V row -- for token substream (w / HGW): substreams take interleaved
-// runs of U list entries, and are merged in substream order at the end.
-// Then the document's split partial states (written by the document kernel
-// or by the per-question baseline) are merged in split order, followed by
-// this stream's own state, and the output row is written.  The fixed merge
-// order makes the result bitwise reproducible.
+// Workgroup = one stream x one group of GW heads (a contiguous GW*d-element
+// slice of every K/V row, so each wave-wide 16-byte load is 1 KB contiguous).
+// Its 4 waves are token substreams: substream w takes list entries
+// [w*U, w*U + U), [w*U + 4U, ...), ..., keeps its own online-softmax state,
+// and the states are merged in substream order.  Then the document's split
+// partial states (from the document kernel, or from the per-question
+// baseline) are merged in split order, followed by the stream's own state,
+// and the output slice is written.  Splitting streams by head group gives
+// P * H/GW small workgroups, which spread streams of different tail lengths
+// evenly over the CUs.  The fixed merge order makes the result bitwise
+// reproducible.
 #include <math.h>
 
 #include "pp_internal.h"
@@ -26,8 +27,12 @@
 namespace pp {
 namespace {
 
-constexpr int kTailThreads = 512;  // 8 waves
+constexpr int kTailThreads = 256;  // 4 waves = 4 token substreams of one head group
+constexpr int kTailNTS = kTailThreads / 64;
 constexpr int kTailU = 4;          // list entries per substream step (loads in flight)
+constexpr int kTailScanU = 64;     // stream ids per thread per compaction chunk (16K-slot chunks)
+constexpr int kTailCap = 2048;     // visible slots compacted per round
+constexpr int kMergeBatch = 4;     // document split partials loaded per batch in the merge
 constexpr int kTailNI = 2;         // 16-byte vectors per lane per K row
 
 template <typename T, int D>
@@ -35,7 +40,7 @@ struct TailShape {
   static constexpr int VEC = 16 / (int)sizeof(T);  // elements per 16-byte vector
   static constexpr int LPH = D / VEC;              // lanes sharing one head
   static constexpr int HPI = 64 / LPH;             // heads per wave-wide vector load
-  static constexpr int GW = kTailNI * HPI;         // heads per wave
+  static constexpr int GW = kTailNI * HPI;         // heads per workgroup
 };
 
 template <typename T>
@@ -66,11 +71,12 @@ __device__ __forceinline__ u32x4 from_f32<float>(const float* f) {
 }
 
 // (M, Ls, A) <- merge with (m2, l2, A2); states with m = -inf are empty.
+// Branch-free, so loads of later states are not held behind this one.
 template <int VEC>
 __device__ __forceinline__ void merge_state(float& M, float& Ls, float* A, float m2, float l2, const float* A2) {
   const float Mn = fmaxf(M, m2);
-  if (Mn == -INFINITY) return;
-  const float a = fast_exp2(M - Mn), b = fast_exp2(m2 - Mn);
+  const float ref = Mn == -INFINITY ? 0.f : Mn;  // both empty: weights exp2(-inf) = 0
+  const float a = fast_exp2(M - ref), b = fast_exp2(m2 - ref);
   Ls = Ls * a + l2 * b;
 #pragma unroll
   for (int e = 0; e < VEC; ++e) A[e] = A[e] * a + A2[e] * b;
@@ -80,39 +86,37 @@ __device__ __forceinline__ void merge_state(float& M, float& Ls, float* A, float
 template <typename T, int D>
 __global__ __launch_bounds__(kTailThreads) void tail_merge_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ sid,
-    int64_t seq_len, int P, int H, float c, const int32_t* __restrict__ doc_len_ptr, int n_splits,
-    const float* __restrict__ part_o, const float2* __restrict__ part_ml, T* __restrict__ out, int HGW) {
+    int64_t seq_len, int P, int H, float c, const int32_t* __restrict__ plan_parts, int n_splits,
+    const float* __restrict__ part_o, const float2* __restrict__ part_ml, T* __restrict__ out) {
   using S = TailShape<T, D>;
   constexpr int VEC = S::VEC, LPH = S::LPH, HPI = S::HPI, GW = S::GW;
-  constexpr int NW = kTailThreads / 64;
   constexpr int RED = kTailNI * (VEC + 2);  // floats per lane in the substream merge
 
-  __shared__ int list[kCollectChunk];
-  __shared__ int scan[NW + 1];
-  __shared__ float red[(NW - 1) * RED * 64];
+  __shared__ int list[kTailCap];
+  __shared__ int scan[kTailNTS + 2];
+  __shared__ float red[(kTailNTS - 1) * RED * 64];
 
-  const int s = blockIdx.x;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int NTS = NW / HGW;
-  const int hgl = wave % HGW, ts = wave / HGW;
-  const int hg = blockIdx.y * HGW + hgl;
+  const int s = blockIdx.x, hg = blockIdx.y;
+  const int tid = threadIdx.x, ts = tid >> 6, lane = tid & 63;
   const int64_t row = (int64_t)H * D;
 
-  int head[kTailNI], d0[kTailNI];
+  // lane covers head head[i], dims d0[i] .. +VEC of its 16-byte vector i;
+  // lanes of heads past H use head 0 for their (unconditional) loads and
+  // discard the results
+  int head[kTailNI], safe_head[kTailNI], d0[kTailNI];
   bool valid[kTailNI];
 #pragma unroll
   for (int i = 0; i < kTailNI; ++i) {
     head[i] = hg * GW + i * HPI + lane / LPH;
     d0[i] = (lane % LPH) * VEC;
     valid[i] = head[i] < H;
+    safe_head[i] = valid[i] ? head[i] : 0;
   }
 
   float qv[kTailNI][VEC], mm[kTailNI], ll[kTailNI], acc[kTailNI][VEC];
 #pragma unroll
   for (int i = 0; i < kTailNI; ++i) {
-    u32x4 w = u32x4{0u, 0u, 0u, 0u};
-    if (valid[i]) w = *reinterpret_cast<const u32x4*>(q + ((int64_t)s * H + head[i]) * D + d0[i]);
-    to_f32<T>(w, qv[i]);
+    to_f32<T>(*reinterpret_cast<const u32x4*>(q + ((int64_t)s * H + safe_head[i]) * D + d0[i]), qv[i]);
     mm[i] = -INFINITY;
     ll[i] = 0.f;
 #pragma unroll
@@ -120,30 +124,27 @@ __global__ __launch_bounds__(kTailThreads) void tail_merge_kernel(
   }
 
   // ---- own slots (and late document slots), gathered ------------------------
-  int64_t from = *doc_len_ptr;
+  int64_t from = doc_prefix_from_parts(plan_parts, seq_len);
   while (from < seq_len) {
     int64_t next;
-    const int n = collect_visible<kTailThreads>(sid, from, seq_len, s + 1, list, kCollectChunk, &next, scan);
-    for (int base = ts * kTailU; base < n; base += NTS * kTailU) {
+    const int n = collect_visible<kTailThreads, kTailScanU>(sid, from, seq_len, s + 1, list, kTailCap, &next, scan);
+    for (int base = ts * kTailU; base < n; base += kTailNTS * kTailU) {
+      // unconditional loads (entries past the end re-read the last one) so
+      // that all of them are in flight together
       u32x4 kr[kTailU][kTailNI], vr[kTailU][kTailNI];
 #pragma unroll
       for (int u = 0; u < kTailU; ++u) {
-        const int j = base + u < n ? list[base + u] : -1;
+        const int j = list[min(base + u, n - 1)];
 #pragma unroll
         for (int i = 0; i < kTailNI; ++i) {
-          if (j >= 0 && valid[i]) {
-            const int64_t off = (int64_t)j * row + (int64_t)head[i] * D + d0[i];
-            kr[u][i] = *reinterpret_cast<const u32x4*>(k + off);
-            vr[u][i] = *reinterpret_cast<const u32x4*>(v + off);
-          } else {
-            kr[u][i] = u32x4{0u, 0u, 0u, 0u};
-            vr[u][i] = u32x4{0u, 0u, 0u, 0u};
-          }
+          const int64_t off = (int64_t)j * row + (int64_t)safe_head[i] * D + d0[i];
+          kr[u][i] = *reinterpret_cast<const u32x4*>(k + off);
+          vr[u][i] = *reinterpret_cast<const u32x4*>(v + off);
         }
       }
 #pragma unroll
       for (int u = 0; u < kTailU; ++u) {
-        if (base + u >= n) break;  // uniform across the workgroup
+        if (base + u >= n) break;  // uniform across the wave
 #pragma unroll
         for (int i = 0; i < kTailNI; ++i) {
           float kf[VEC], vf[VEC];
@@ -170,7 +171,7 @@ __global__ __launch_bounds__(kTailThreads) void tail_merge_kernel(
 
   // ---- merge token substreams (fixed order 0, 1, ..., NTS-1) -----------------
   if (ts > 0) {
-    float* r = red + (size_t)((ts - 1) * HGW + hgl) * RED * 64;
+    float* r = red + (size_t)(ts - 1) * RED * 64;
 #pragma unroll
     for (int i = 0; i < kTailNI; ++i) {
       r[(i * (VEC + 2) + 0) * 64 + lane] = mm[i];
@@ -180,9 +181,10 @@ __global__ __launch_bounds__(kTailThreads) void tail_merge_kernel(
     }
   }
   __syncthreads();
-  if (ts != 0 || hg * GW >= H) return;
-  for (int t2 = 1; t2 < NTS; ++t2) {
-    const float* r = red + (size_t)((t2 - 1) * HGW + hgl) * RED * 64;
+  if (ts != 0) return;
+#pragma unroll
+  for (int t2 = 1; t2 < kTailNTS; ++t2) {
+    const float* r = red + (size_t)(t2 - 1) * RED * 64;
 #pragma unroll
     for (int i = 0; i < kTailNI; ++i) {
       float a2[VEC];
@@ -193,29 +195,37 @@ __global__ __launch_bounds__(kTailThreads) void tail_merge_kernel(
   }
 
   // ---- merge document splits in order, then this stream's own state ---------
+  // Partials are loaded kMergeBatch splits at a time (indices past the last
+  // split re-read split 0 and are skipped), then merged in split order.
 #pragma unroll
   for (int i = 0; i < kTailNI; ++i) {
-    if (!valid[i]) continue;
     float M = -INFINITY, Ls = 0.f, A[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) A[e] = 0.f;
-#pragma unroll 4
-    for (int sp = 0; sp < n_splits; ++sp) {
-      const int64_t sh = ((int64_t)sp * P + s) * H + head[i];
-      const float2 ml = part_ml[sh];
-      float o2[VEC];
-      const float* src = part_o + sh * D + d0[i];
+    for (int sp0 = 0; sp0 < n_splits; sp0 += kMergeBatch) {
+      float2 ml[kMergeBatch];
+      float o2[kMergeBatch][VEC];
 #pragma unroll
-      for (int e = 0; e < VEC; e += 4) {
-        const float4 x = *reinterpret_cast<const float4*>(src + e);
-        o2[e] = x.x;
-        o2[e + 1] = x.y;
-        o2[e + 2] = x.z;
-        o2[e + 3] = x.w;
+      for (int b = 0; b < kMergeBatch; ++b) {
+        const int sp = sp0 + b < n_splits ? sp0 + b : 0;
+        const int64_t sh = ((int64_t)sp * P + s) * H + safe_head[i];
+        ml[b] = part_ml[sh];
+        const float* src = part_o + sh * D + d0[i];
+#pragma unroll
+        for (int e = 0; e < VEC; e += 4) {
+          const float4 x = *reinterpret_cast<const float4*>(src + e);
+          o2[b][e] = x.x;
+          o2[b][e + 1] = x.y;
+          o2[b][e + 2] = x.z;
+          o2[b][e + 3] = x.w;
+        }
       }
-      merge_state<VEC>(M, Ls, A, ml.x, ml.y, o2);
+#pragma unroll
+      for (int b = 0; b < kMergeBatch; ++b)
+        if (sp0 + b < n_splits) merge_state<VEC>(M, Ls, A, ml[b].x, ml[b].y, o2[b]);
     }
     merge_state<VEC>(M, Ls, A, mm[i], ll[i], acc[i]);
+    if (!valid[i]) continue;
     float res[VEC];
     const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
 #pragma unroll
@@ -228,13 +238,10 @@ template <typename T, int D>
 hipError_t launch_tail_t(int n_splits, const void* q, const void* k, const void* v, const int32_t* sid,
                          int64_t seq_len, int P, int H, float c, const Workspace& ws, void* out, hipStream_t stream) {
   using S = TailShape<T, D>;
-  const int nhg = (H + S::GW - 1) / S::GW;
-  int hgw = 1;
-  while (hgw * 2 <= nhg && hgw * 2 <= kTailThreads / 64) hgw *= 2;
-  const dim3 grid(P, (nhg + hgw - 1) / hgw);
+  const dim3 grid(P, (H + S::GW - 1) / S::GW);
   tail_merge_kernel<T, D><<<grid, kTailThreads, 0, stream>>>(
-      static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), sid, seq_len, P, H, c, ws.doc_len,
-      n_splits, ws.part_o, ws.part_ml, static_cast<T*>(out), hgw);
+      static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), sid, seq_len, P, H, c, ws.plan_parts,
+      n_splits, ws.part_o, ws.part_ml, static_cast<T*>(out));
   return hipGetLastError();
 }
 

@@ -92,14 +92,17 @@ def test_workspace_bytes():
 
 def test_plan_validation():
     lib = pp.raw()
-    assert lib.pp_attn_plan(None, 10, 2, OUT, WS, K, 4, None) == pp.PP_ERR_INVALID_ARG
-    assert lib.pp_attn_plan(SID, 0, 2, OUT, WS, K, 4, None) == pp.PP_ERR_INVALID_ARG
-    assert lib.pp_attn_plan(SID, 10, 0, OUT, WS, K, 4, None) == pp.PP_ERR_INVALID_ARG
-    assert lib.pp_attn_plan(SID, 10, 2, None, WS, K, 4, None) == pp.PP_ERR_INVALID_ARG
-    assert lib.pp_attn_plan(SID, 10, 2, OUT, None, K, 4, None) == pp.PP_ERR_INVALID_ARG
-    assert lib.pp_attn_plan(SID, 10, 2, OUT, WS, None, 4, None) == pp.PP_ERR_INVALID_ARG
-    assert lib.pp_attn_plan(SID, 10, 2, OUT, WS, K, -1, None) == pp.PP_ERR_INVALID_ARG
-    assert lib.pp_attn_plan(SID + 4, 10, 2, OUT, WS, K, 4, None) == pp.PP_ERR_INVALID_ARG
+    n = pp.PP_PLAN_WORKSPACE_BYTES
+    assert lib.pp_attn_plan(None, 10, 2, OUT, WS, K, 4, V, n, None) == pp.PP_ERR_INVALID_ARG
+    assert lib.pp_attn_plan(SID, 0, 2, OUT, WS, K, 4, V, n, None) == pp.PP_ERR_INVALID_ARG
+    assert lib.pp_attn_plan(SID, 10, 0, OUT, WS, K, 4, V, n, None) == pp.PP_ERR_INVALID_ARG
+    assert lib.pp_attn_plan(SID, 10, 2, None, WS, K, 4, V, n, None) == pp.PP_ERR_INVALID_ARG
+    assert lib.pp_attn_plan(SID, 10, 2, OUT, None, K, 4, V, n, None) == pp.PP_ERR_INVALID_ARG
+    assert lib.pp_attn_plan(SID, 10, 2, OUT, WS, None, 4, V, n, None) == pp.PP_ERR_INVALID_ARG
+    assert lib.pp_attn_plan(SID, 10, 2, OUT, WS, K, -1, V, n, None) == pp.PP_ERR_INVALID_ARG
+    assert lib.pp_attn_plan(SID + 4, 10, 2, OUT, WS, K, 4, V, n, None) == pp.PP_ERR_INVALID_ARG
+    assert lib.pp_attn_plan(SID, 10, 2, OUT, WS, K, 4, None, n, None) == pp.PP_ERR_WORKSPACE
+    assert lib.pp_attn_plan(SID, 10, 2, OUT, WS, K, 4, V, 100, None) == pp.PP_ERR_WORKSPACE
 
 
 def test_python_binding_rejects_cpu_tensors():
