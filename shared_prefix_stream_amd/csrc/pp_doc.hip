@@ -53,16 +53,15 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 template <int D, int QB, int NW>
 struct DocTile {
-  // Document slots per tile: 64, or 32 for the widest per-wave query tile at
-  // d = 128, whose accumulators (64 queries x 128 dims per wave) leave the
-  // fewest registers.
-  static constexpr int NK = (D == 128 && QB == 4) ? 32 : 64;
+  // Document slots per tile: 64, or more when needed for every wave to issue
+  // at least one 1 KB direct load per tile (128 at d = 64 with 16 waves).
+  static constexpr int NK = (1024 * NW) / (D * 2) > 64 ? (1024 * NW) / (D * 2) : 64;
   static constexpr int THREADS = 64 * NW;
   static constexpr int ROWB = D * 2;                 // bytes of one K or V row (one head)
   static constexpr int CPR = D / 8;                  // 16-byte chunks per row
   static constexpr int TILE_BYTES = NK * ROWB;       // K (or V) tile
   static constexpr int STAGE_BYTES = 2 * TILE_BYTES;
-  static constexpr int NS = STAGE_BYTES <= 16384 ? 4 : 3;  // pipeline depth (stages in LDS)
+  static constexpr int NS = 4;                       // LDS ring stages (see the pipeline below)
   static constexpr int ROWS_PER_KB = 1024 / ROWB;    // rows one wave-wide 16-byte load fills
   static constexpr int NLD = TILE_BYTES / 1024 / NW;  // direct loads per thread per tile (K or V)
   static_assert(NLD >= 1 && TILE_BYTES % (1024 * NW) == 0, "tile shape");
@@ -169,23 +168,29 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
     }
   }
 
+  // O^T accumulators, and the softmax denominators: l is accumulated on the
+  // matrix cores as an extra 16-row block whose A operand is all ones, so
+  // every row (and lane) holds sum_k bf16(p_k) for its query -- the same
+  // rounded weights the numerator uses.
   f32x4 o[QB][DB];
-  float m[QB], l[QB];
+  f32x4 lsum[QB];
+  float m[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     m[qb] = -INFINITY;
-    l[qb] = 0.f;
+    lsum[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 
   // Direct global->LDS loads of tile t into stage st.  Wave w's i-th load
   // fills 1 KB block (i*NW + w) of the K and of the V tile; rows past the
   // split's end re-read its last row (finite data, masked out of the scores).
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t ring_base = lds_addr(&ring[0][0]);
-  auto issue = [&](int t, int st) {
-    const uint32_t ks = ring_base + st * TL::STAGE_BYTES;
+  auto issue = [&](int t) {
+    const uint32_t ks = ring_base + ((t - t0) % NS) * TL::STAGE_BYTES;
     const uint32_t vs = ks + TL::TILE_BYTES;
     const int kbase = t * NK;
 #pragma unroll
@@ -199,45 +204,42 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
     }
   };
 
-#pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
-    if (t0 + s < t1) issue(t0 + s, s);
-
-  for (int t = t0; t < t1; ++t) {
-    const int st = (t - t0) % NS;
-    // tile t's loads are complete once at most the younger tiles' remain
-    const int younger = min(NS - 2, t1 - 1 - t);
-    if (younger >= 2) wait_vmcnt<2 * 2 * NLD>();
-    else if (younger == 1) wait_vmcnt<2 * NLD>();
-    else wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();        // every wave's loads of tile t are in LDS, and
-    asm volatile("" ::: "memory");       // every wave is done reading stage (t-1) % NS
-    if (t + NS - 1 < t1) issue(t + NS - 1, (t - t0 + NS - 1) % NS);
-
-    const unsigned char* ks = ring[st];
-    const unsigned char* vs = ring[st] + TL::TILE_BYTES;
-    const int kbase = t * NK;
-
-    // ---- S^T = K Q^T -------------------------------------------------------
-    f32x4 s[QB][KB];
+  // ---- S^T = K Q^T for tile t ------------------------------------------------
+  // The K fragments of dim chunk kc+1 are read from LDS while the MFMAs of
+  // chunk kc run (two register buffers), so LDS latency stays hidden.
+  f32x4 s[QB][KB];
+  auto qk = [&](int t) {
+    const unsigned char* ks = ring[(t - t0) % NS];
+    auto kfrag = [&](int kc, int kb) {
+      const int key = key_of(kb, ln);
+      const int col = kc * 4 + lg;
+      return *reinterpret_cast<const bf16x8*>(ks + key * ROWB + ((col ^ swz_k<D>(key)) * 16));
+    };
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) s[qb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 a[2][KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) a[0][kb] = kfrag(0, kb);
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
+      if (kc + 1 < KC) {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const int key = key_of(kb, ln);
-        const int col = kc * 4 + lg;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + key * ROWB + ((col ^ swz_k<D>(key)) * 16));
+        for (int kb = 0; kb < KB; ++kb) a[(kc + 1) & 1][kb] = kfrag(kc + 1, kb);
+      }
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
-          s[qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[qb][kc], s[qb][kb], 0, 0, 0);
-      }
+          s[qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kc & 1][kb], qf[qb][kc], s[qb][kb], 0, 0, 0);
     }
+  };
 
-    // ---- online softmax, base 2, lazy rescale ------------------------------
+  // ---- online softmax of tile t (base 2, lazy rescale) -> packed P^T --------
+  uint32_t pb[QB][CH][4];  // P^T as packed bf16 pairs: the P.V B operand
+  auto softmax = [&](int t) {
+    const int kbase = t * NK;
     if (kbase + NK > key_end) {  // ragged last tile of the split (uniform)
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
@@ -270,25 +272,18 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
         const float mn = fmaxf(m[qb], tmax[qb]);
         const float alpha = fast_exp2(m[qb] - mn);
         m[qb] = mn;
-        l[qb] *= alpha;
+        lsum[qb] *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db) o[qb][db] *= alpha;
       }
     }
-    uint32_t pb[QB][CH][4];  // P^T as packed bf16 pairs: the P.V B operand
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const float mneg = -m[qb];
-      float psum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = fast_exp2(fmaf(s[qb][kb][i], cabs, mneg));
-          s[qb][kb][i] = p;
-          psum += p;
-        }
-      l[qb] += psum;
+        for (int i = 0; i < 4; ++i) s[qb][kb][i] = fast_exp2(fmaf(s[qb][kb][i], cabs, mneg));
 #pragma unroll
       for (int ch = 0; ch < CH; ++ch) {
         pb[qb][ch][0] = pack_bf16x2(s[qb][2 * ch][0], s[qb][2 * ch][1]);
@@ -297,37 +292,92 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
         pb[qb][ch][3] = pack_bf16x2(s[qb][2 * ch + 1][2], s[qb][2 * ch + 1][3]);
       }
     }
+  };
 
-    // ---- O^T += V^T P^T ----------------------------------------------------
+  // ---- O^T += V^T P^T for tile t (and the row sums, on the matrix cores) ----
+  // V operands are read with the transposing LDS load two (chunk, dim-block)
+  // steps ahead of the MFMAs that use them.
+  auto pv = [&](int t) {
+    const unsigned char* vs = ring[(t - t0) % NS] + TL::TILE_BYTES;
+    auto vfrag = [&](int ch, int db) {
+      // lane (ln, lg) points at row 32ch + 8lg + 4half + ln/4, dims db*16 + 4(ln%4) .. +4
+      bf16x4 half2[2];
 #pragma unroll
-    for (int ch = 0; ch < CH; ++ch) {
+      for (int half = 0; half < 2; ++half) {
+        const int key = 32 * ch + 8 * lg + 4 * half + (ln >> 2);
+        const int dim = db * 16 + 4 * (ln & 3);
+        const int chunk = dim >> 3;
+        const unsigned char* src = vs + key * ROWB + ((chunk ^ swz_v<D>(key)) * 16) + (dim & 7) * 2;
+        half2[half] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(src));
+      }
+      return __builtin_shufflevector(half2[0], half2[1], 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    constexpr int NSTEP = CH * DB;
+    constexpr int AHEAD = 2;
+    bf16x8 va[AHEAD + 1];
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        // lane (ln, lg) points at row 32ch + 8lg + 4half + ln/4, dims db*16 + 4(ln%4) .. +4
-        bf16x4 half2[2];
+    for (int i = 0; i < AHEAD; ++i) va[i] = vfrag(i / DB, i % DB);
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int key = 32 * ch + 8 * lg + 4 * half + (ln >> 2);
-          const int dim = db * 16 + 4 * (ln & 3);
-          const int chunk = dim >> 3;
-          const unsigned char* src = vs + key * ROWB + ((chunk ^ swz_v<D>(key)) * 16) + (dim & 7) * 2;
-          half2[half] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (__attribute__((address_space(3))) bf16x4*)(src));
-        }
-        const bf16x8 a = __builtin_shufflevector(half2[0], half2[1], 0, 1, 2, 3, 4, 5, 6, 7);
+    for (int i = 0; i < NSTEP; ++i) {
+      const int ch = i / DB, db = i % DB;
+      if (i + AHEAD < NSTEP) va[(i + AHEAD) % (AHEAD + 1)] = vfrag((i + AHEAD) / DB, (i + AHEAD) % DB);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const u32x4 bw = u32x4{pb[qb][ch][0], pb[qb][ch][1], pb[qb][ch][2], pb[qb][ch][3]};
+        o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[i % (AHEAD + 1)], __builtin_bit_cast(bf16x8, bw),
+                                                            o[qb][db], 0, 0, 0);
+      }
+      if (db == DB - 1) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
           const u32x4 bw = u32x4{pb[qb][ch][0], pb[qb][ch][1], pb[qb][ch][2], pb[qb][ch][3]};
-          o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, bw), o[qb][db], 0, 0, 0);
+          lsum[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, __builtin_bit_cast(bf16x8, bw), lsum[qb], 0, 0, 0);
         }
       }
     }
+  };
+
+  // ---- pipeline -----------------------------------------------------------------
+  // Tile t is loaded two iterations ahead (ring of NS = 4 stages: tiles t-1
+  // and t are read in iteration t, t+1 and t+2 are in flight).  Waves of
+  // group A (all waves, or the first half when two waves share a SIMD) run
+  //     [P.V(t-1), QK(t)] (matrix cores) then softmax(t) (vector ALUs);
+  // group B runs the same work shifted by half an iteration,
+  //     softmax(t-1) then [P.V(t-1), QK(t)],
+  // so after each barrier one wave of every SIMD is on the matrix cores while
+  // the other is on the vector ALUs.
+  static_assert(NS == 4, "two tiles ahead plus two tiles in use");
+  // waves w and w + 4 share a SIMD: alternate groups by (w / 4)
+  const bool grp_b = NW >= 8 && ((wave >> 2) & 1);
+  if (t0 < t1) {
+    issue(t0);
+    if (t0 + 1 < t1) issue(t0 + 1);
+    for (int t = t0; t < t1; ++t) {
+      if (t + 1 < t1) wait_vmcnt<2 * NLD>();  // tile t landed; t+1 may be in flight
+      else wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();   // every wave's loads of tile t are in LDS, and every
+      asm volatile("" ::: "memory");  // wave is done with tile t-2 (its stage is reused next)
+      if (t + 2 < t1) issue(t + 2);
+      if (!grp_b) {
+        if (t > t0) pv(t - 1);
+        qk(t);
+        softmax(t);
+      } else {
+        if (t > t0) {
+          softmax(t - 1);
+          pv(t - 1);
+        }
+        qk(t);
+      }
+    }
+    if (grp_b) softmax(t1 - 1);
+    pv(t1 - 1);
   }
 
   // ---- partial state of this split -------------------------------------------
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float lt = sum_xor32(sum_xor16(l[qb]));
+    const float lt = lsum[qb][0];
     const int p = q0 + qb * 16 + ln;
     if (p < P) {
       const int64_t sh = ((int64_t)split * P + p) * H + h;
@@ -426,6 +476,7 @@ DocPlan choose_doc_plan(int64_t seq_len, int P, int H, int d, pp_dtype_t dtype, 
   if (dtype == PP_BF16) {
     // 16-query blocks per wave and waves per workgroup: (1, 4) for P <= 64,
     // (2, 4) for P <= 128, else (2, 8): 256 queries of a head per workgroup
+    // as 8 waves of 32 queries, two waves per SIMD
     pl.qb = P <= 64 ? 1 : 2;
     pl.nw = P <= 128 ? 4 : 8;
     const int per_wg = 16 * pl.qb * pl.nw;
@@ -457,14 +508,16 @@ hipError_t launch_doc(const DocPlan& pl, const void* q, const void* k, const voi
 #define PP_DOC_LAUNCH(DD, QQ, WW)                                                                      \
   doc_mfma_bf16_kernel<DD, QQ, WW><<<grid, 64 * WW, 0, stream>>>(qq, kk, vv, P, H, c, ws.plan_parts, \
                                                                   seq_len, pl.n_splits, ws.part_o, ws.part_ml)
-    if (d == 128) {
-      if (pl.qb == 1) PP_DOC_LAUNCH(128, 1, 4);
-      else if (pl.nw == 4) PP_DOC_LAUNCH(128, 2, 4);
-      else PP_DOC_LAUNCH(128, 2, 8);
-    } else {
-      if (pl.qb == 1) PP_DOC_LAUNCH(64, 1, 4);
-      else if (pl.nw == 4) PP_DOC_LAUNCH(64, 2, 4);
-      else PP_DOC_LAUNCH(64, 2, 8);
+    // dispatch on the exact (d, 16-query blocks per wave, waves) triple
+    const int cfg = d * 10000 + pl.qb * 100 + pl.nw;
+    switch (cfg) {
+      case 1280104: PP_DOC_LAUNCH(128, 1, 4); break;
+      case 1280204: PP_DOC_LAUNCH(128, 2, 4); break;
+      case 1280208: PP_DOC_LAUNCH(128, 2, 8); break;
+      case 640104: PP_DOC_LAUNCH(64, 1, 4); break;
+      case 640204: PP_DOC_LAUNCH(64, 2, 4); break;
+      case 640208: PP_DOC_LAUNCH(64, 2, 8); break;
+      default: return hipErrorInvalidConfiguration;
     }
 #undef PP_DOC_LAUNCH
   } else {

@@ -48,11 +48,11 @@ inline Workspace carve_workspace(void* ws, int n_splits, int64_t P, int64_t H) {
 // --------------------------------------------------------- device helpers ---
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
 
-// round-to-nearest-even fp32 -> bf16 (hardware v_cvt_pk_bf16_f32 on gfx950)
+// round-to-nearest-even fp32 -> bf16 pair (one v_cvt_pk_bf16_f32 on gfx950)
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(unsigned short, a) |
-         ((uint32_t)__builtin_bit_cast(unsigned short, b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -105,6 +105,9 @@ __device__ __forceinline__ int doc_prefix_from_parts(const int32_t* __restrict__
   int x = parts[threadIdx.x & 63];
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) x = min(x, __shfl_xor(x, o));
+  // every lane holds the minimum now; make that visible to the compiler so
+  // loops bounded by it stay on the scalar unit
+  x = __builtin_amdgcn_readfirstlane(x);
   return (int64_t)x < seq_len ? x : (int)seq_len;
 }
 
@@ -151,9 +154,12 @@ __device__ int collect_visible(const int32_t* __restrict__ sid, int64_t from, in
       const int ids[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
+        // bitwise (not short-circuit) operators: the element is always read,
+        // so the 16-byte load is never split into guarded narrower loads
         const int64_t j = jg + e;
-        const bool vis = (j >= from) && (j < seq_len) && (ids[e] == 0 || ids[e] == s1);
-        match |= (vis ? 1ull : 0ull) << (4 * g + e);
+        const unsigned vis = (unsigned)(j >= from) & (unsigned)(j < seq_len) &
+                             ((unsigned)(ids[e] == 0) | (unsigned)(ids[e] == s1));
+        match |= (uint64_t)vis << (4 * g + e);
       }
     }
     const int c = __popcll(match);

@@ -35,8 +35,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_doclen_kernel(const int32_t
       const int4 x = *reinterpret_cast<const int4*>(sid + (jg < last_gran ? jg : last_gran));
       const int ids[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
-      for (int e = 3; e >= 0; --e)
-        if (jg + e < seq_len && ids[e] != 0) first = (int)(jg + e);
+      for (int e = 3; e >= 0; --e) {
+        // bitwise test so every element is read (the load is never split)
+        const unsigned hit = (unsigned)(jg + e < seq_len) & (unsigned)(ids[e] != 0);
+        first = hit ? (int)(jg + e) : first;
+      }
     }
     if (first != 0x7fffffff) atomicMin(&found, first);
     __syncthreads();

@@ -11,15 +11,15 @@
 //
 // Workgroup = one stream x one group of GW heads (a contiguous GW*d-element
 // slice of every K/V row, so each wave-wide 16-byte load is 1 KB contiguous).
-// Its 4 waves are token substreams: substream w takes list entries
-// [w*U, w*U + U), [w*U + 4U, ...), ..., keeps its own online-softmax state,
-// and the states are merged in substream order.  Then the document's split
-// partial states (from the document kernel, or from the per-question
-// baseline) are merged in split order, followed by the stream's own state,
-// and the output slice is written.  Splitting streams by head group gives
-// P * H/GW small workgroups, which spread streams of different tail lengths
-// evenly over the CUs.  The fixed merge order makes the result bitwise
-// reproducible.
+// Its 4 waves are substreams.  Substream w first merges the document split
+// partial states w, w+4, w+8, ... (written by the document kernel, or by the
+// per-question baseline) -- their loads are issued at kernel start, so they
+// overlap the slot compaction -- then folds in list entries [w*U, w*U + U),
+// [w*U + 4U, ...), ... with an online softmax.  The four states are merged
+// in substream order and the output slice is written.  Every step has a
+// fixed order, so the result is bitwise reproducible.  Splitting streams by
+// head group gives P * H/GW small workgroups, which spread streams of
+// different tail lengths evenly over the CUs.
 #include <math.h>
 
 #include "pp_internal.h"
@@ -32,7 +32,7 @@ constexpr int kTailNTS = kTailThreads / 64;
 constexpr int kTailU = 4;          // list entries per substream step (loads in flight)
 constexpr int kTailScanU = 64;     // stream ids per thread per compaction chunk (16K-slot chunks)
 constexpr int kTailCap = 2048;     // visible slots compacted per round
-constexpr int kMergeBatch = 4;     // document split partials loaded per batch in the merge
+constexpr int kMergeBatch = 2;     // document split partials a substream loads at once
 constexpr int kTailNI = 2;         // 16-byte vectors per lane per K row
 
 template <typename T, int D>
@@ -123,6 +123,38 @@ __global__ __launch_bounds__(kTailThreads) void tail_merge_kernel(
     for (int e = 0; e < VEC; ++e) acc[i][e] = 0.f;
   }
 
+  // ---- this substream's share of the document split partials ---------------
+  // splits ts, ts + NTS, ...; loaded kMergeBatch at a time (indices past the
+  // last split re-read split 0 and are skipped), merged in split order
+  for (int sp0 = ts; sp0 < n_splits; sp0 += kTailNTS * kMergeBatch) {
+    float2 ml[kMergeBatch][kTailNI];
+    float o2[kMergeBatch][kTailNI][VEC];
+#pragma unroll
+    for (int b = 0; b < kMergeBatch; ++b) {
+      const int spb = sp0 + b * kTailNTS;
+      const int sp = spb < n_splits ? spb : 0;
+#pragma unroll
+      for (int i = 0; i < kTailNI; ++i) {
+        const int64_t sh = ((int64_t)sp * P + s) * H + safe_head[i];
+        ml[b][i] = part_ml[sh];
+        const float* src = part_o + sh * D + d0[i];
+#pragma unroll
+        for (int e = 0; e < VEC; e += 4) {
+          const float4 x = *reinterpret_cast<const float4*>(src + e);
+          o2[b][i][e] = x.x;
+          o2[b][i][e + 1] = x.y;
+          o2[b][i][e + 2] = x.z;
+          o2[b][i][e + 3] = x.w;
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < kMergeBatch; ++b)
+      if (sp0 + b * kTailNTS < n_splits)
+#pragma unroll
+        for (int i = 0; i < kTailNI; ++i) merge_state<VEC>(mm[i], ll[i], acc[i], ml[b][i].x, ml[b][i].y, o2[b][i]);
+  }
+
   // ---- own slots (and late document slots), gathered ------------------------
   int64_t from = doc_prefix_from_parts(plan_parts, seq_len);
   while (from < seq_len) {
@@ -194,42 +226,14 @@ __global__ __launch_bounds__(kTailThreads) void tail_merge_kernel(
     }
   }
 
-  // ---- merge document splits in order, then this stream's own state ---------
-  // Partials are loaded kMergeBatch splits at a time (indices past the last
-  // split re-read split 0 and are skipped), then merged in split order.
+  // ---- write ----------------------------------------------------------------
 #pragma unroll
   for (int i = 0; i < kTailNI; ++i) {
-    float M = -INFINITY, Ls = 0.f, A[VEC];
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) A[e] = 0.f;
-    for (int sp0 = 0; sp0 < n_splits; sp0 += kMergeBatch) {
-      float2 ml[kMergeBatch];
-      float o2[kMergeBatch][VEC];
-#pragma unroll
-      for (int b = 0; b < kMergeBatch; ++b) {
-        const int sp = sp0 + b < n_splits ? sp0 + b : 0;
-        const int64_t sh = ((int64_t)sp * P + s) * H + safe_head[i];
-        ml[b] = part_ml[sh];
-        const float* src = part_o + sh * D + d0[i];
-#pragma unroll
-        for (int e = 0; e < VEC; e += 4) {
-          const float4 x = *reinterpret_cast<const float4*>(src + e);
-          o2[b][e] = x.x;
-          o2[b][e + 1] = x.y;
-          o2[b][e + 2] = x.z;
-          o2[b][e + 3] = x.w;
-        }
-      }
-#pragma unroll
-      for (int b = 0; b < kMergeBatch; ++b)
-        if (sp0 + b < n_splits) merge_state<VEC>(M, Ls, A, ml[b].x, ml[b].y, o2[b]);
-    }
-    merge_state<VEC>(M, Ls, A, mm[i], ll[i], acc[i]);
     if (!valid[i]) continue;
     float res[VEC];
-    const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+    const float inv = ll[i] > 0.f ? 1.f / ll[i] : 0.f;
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) res[e] = Ls > 0.f ? A[e] * inv : 0.f;
+    for (int e = 0; e < VEC; ++e) res[e] = ll[i] > 0.f ? acc[i][e] * inv : 0.f;
     *reinterpret_cast<u32x4*>(out + ((int64_t)s * H + head[i]) * D + d0[i]) = from_f32<T>(res);
   }
 }
