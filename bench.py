@@ -214,18 +214,19 @@ def main():
     t_s = ms / 1e3
 
     # ---- per-kernel durations from events the library records on its stream --
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    n_st = len(pp.PROFILE_STAGES)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_st + 1)]
     for e in evs:
         e.record()
     torch.cuda.synchronize()
     handles = [e.cuda_event for e in evs]
-    stage_ms = [0.0, 0.0, 0.0]
+    stage_ms = [0.0] * n_st
     n_prof = max(5, min(args.steps, 50))
     for _ in range(n_prof):
         pp.pp_attn_decode_profiled(handles, q, k, v, sid, seq_len=case.seq_len, scale=case.scale, out=out,
                                    workspace=ws)
-        evs[3].synchronize()
-        for i in range(3):
+        evs[n_st].synchronize()
+        for i in range(n_st):
             stage_ms[i] += evs[i].elapsed_time(evs[i + 1])
     stage_us = {name: stage_ms[i] / n_prof * 1e3 for i, name in enumerate(pp.PROFILE_STAGES)}
 
@@ -267,10 +268,11 @@ def main():
     kv = by["doc_kv"] + by["tail_kv"]
     kv_gbs = kv / t_s / 1e9
     doc_gbs = by["doc_kv"] / t_s / 1e9
+    # algorithmic bytes only: the split partials (fp32 workspace) are not counted
     stage_bytes = {
         "plan": by["ids"],
         "document": by["doc_kv"] + by["q"],
-        "own_slots_merge": by["tail_kv"] + by["q"] + by["out"] + by["ids"],
+        "own_slots_merge": by["tail_kv"] + by["q"] + by["out"],
     }
     kernels = {}
     for name, us in stage_us.items():

@@ -139,8 +139,8 @@ pp_status_t pp_attn_decode_profiled(int32_t batched, const void* q, const void* 
                                     size_t workspace_bytes, void* hip_stream, void* const* events,
                                     int32_t n_events);
 
-/* The integer visibility plan that both entry points evaluate on the device,
- * exposed for inspection (the same device code as the attention kernels).
+/* The integer visibility plan that both entry points evaluate on the device
+ * (their first kernel), exposed for inspection: the same device code.
  * Writes, on `hip_stream`:
  *   doc_len_out[0]      length of the leading run of id-0 slots (<= seq_len)
  *   tail_count_out[s]   number of slots j >= doc_len visible to stream s
@@ -148,8 +148,9 @@ pp_status_t pp_attn_decode_profiled(int32_t batched, const void* q, const void* 
  *   tail_slots_out[s*tail_capacity + i]  the first min(count, tail_capacity)
  *                       of those slots, ascending
  * All three are caller-owned device buffers (int32; tail_slots_out may be
- * NULL when tail_capacity is 0); `workspace` is caller-owned device scratch of
- * at least PP_PLAN_WORKSPACE_BYTES.  [Project page, "How it works", item 1.]
+ * NULL when tail_capacity is 0).  `workspace` (at least
+ * PP_PLAN_WORKSPACE_BYTES, caller-owned device memory) is reserved: it is
+ * checked but not written.  [Project page, "How it works", item 1.]
  * Errors as above. */
 #define PP_PLAN_WORKSPACE_BYTES 512
 pp_status_t pp_attn_plan(const int32_t* stream_id, int64_t seq_len, int32_t P,

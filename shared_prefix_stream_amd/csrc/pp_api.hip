@@ -83,7 +83,7 @@ Plan plan_for(int64_t seq_len, int32_t P, int32_t H, int32_t d, pp_dtype_t dtype
 size_t required_bytes(int64_t seq_len, int32_t P, int32_t H, int32_t d, pp_dtype_t dtype) {
   const Plan pl = plan_for(seq_len, P, H, d, dtype, kSizingCus);
   const int n = pl.doc.n_splits > pl.batched_splits ? pl.doc.n_splits : pl.batched_splits;
-  return pp::workspace_bytes_for(n, P, H, d);
+  return pp::workspace_bytes_for(n, P, H, d, seq_len);
 }
 
 enum class Path { kParallel, kBatched };
@@ -115,14 +115,14 @@ pp_status_t decode_impl(Path path, const void* q, const void* k, const void* v, 
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   const float c = (float)((double)scale * 1.4426950408889634074);  // log2(e): softmax in base 2
   const int n_splits = path == Path::kParallel ? pl.doc.n_splits : pl.batched_splits;
-  const pp::Workspace ws = pp::carve_workspace(workspace, n_splits, P, H);
+  const pp::Workspace ws = pp::carve_workspace(workspace, n_splits, P, H, seq_len);
 
   // optional profiling events around the launches
   auto mark = [&](int i) -> hipError_t {
     return events ? hipEventRecord(static_cast<hipEvent_t>(events[i]), stream) : hipSuccess;
   };
   hipError_t e = mark(0);
-  if (e == hipSuccess) e = pp::launch_plan_doclen(sid, seq_len, ws.plan_parts, stream);
+  if (e == hipSuccess) e = pp::launch_plan(sid, seq_len, P, ws.plan, ws.counts, ws.slots, ws.cap, stream);
   if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess) {
     e = path == Path::kParallel ? pp::launch_doc(pl.doc, q, k, v, seq_len, P, H, d, dtype, c, ws, stream)
@@ -200,11 +200,10 @@ pp_status_t pp_attn_plan(const int32_t* stream_id, int64_t seq_len, int32_t P, i
   if (!workspace || workspace_bytes < PP_PLAN_WORKSPACE_BYTES)
     return fail(PP_ERR_WORKSPACE, "pp_attn_plan needs %d bytes of workspace", (int)PP_PLAN_WORKSPACE_BYTES);
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-  const pp::Workspace ws = pp::carve_workspace(workspace, 0, P, 1);
-  hipError_t e = pp::launch_plan_doclen(stream_id, seq_len, ws.plan_parts, stream);
-  if (e == hipSuccess)
-    e = pp::launch_plan_lists(stream_id, seq_len, P, ws.plan_parts, doc_len_out, tail_count_out, tail_slots_out,
-                              tail_capacity, stream);
+  // the workspace argument is reserved: the plan is written straight into
+  // the caller's buffers
+  hipError_t e = pp::launch_plan(stream_id, seq_len, P, doc_len_out, tail_count_out, tail_slots_out, tail_capacity,
+                                 stream);
   if (e != hipSuccess) return fail(PP_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }

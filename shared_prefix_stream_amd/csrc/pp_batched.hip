@@ -56,7 +56,7 @@ __device__ __forceinline__ void merge_b(float& M, float& Ls, float* A, float m2,
 template <typename T, int D>
 __global__ __launch_bounds__(kBThreads) void batched_doc_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, int P, int H, float c,
-    const int32_t* __restrict__ plan_parts, int64_t seq_len, int n_splits, float* __restrict__ part_o,
+    const int32_t* __restrict__ plan, int64_t seq_len, int n_splits, float* __restrict__ part_o,
     float2* __restrict__ part_ml) {
   constexpr int VEC = 16 / (int)sizeof(T);
   constexpr int LPK = D / VEC;   // lanes per slot
@@ -67,7 +67,7 @@ __global__ __launch_bounds__(kBThreads) void batched_doc_kernel(
   const int h = blockIdx.x, split = blockIdx.y, s = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int kg = lane / LPK, dl = lane % LPK;
-  const int64_t L = doc_prefix_from_parts(plan_parts, seq_len);
+  const int64_t L = load_doc_len(plan);
   const int64_t j_begin = split * L / n_splits, j_end = (split + 1) * L / n_splits;
   const int64_t row = (int64_t)H * D;
 
@@ -170,7 +170,7 @@ hipError_t launch_batched_doc(int n_splits, const void* q, const void* k, const 
   const dim3 grid(H, n_splits, P);  // dispatch order: heads, then splits, stream outermost
 #define PP_B_LAUNCH(TT, DD)                                                                                   \
   batched_doc_kernel<TT, DD><<<grid, kBThreads, 0, stream>>>(static_cast<const TT*>(q), static_cast<const TT*>(k), \
-                                                             static_cast<const TT*>(v), P, H, c, ws.plan_parts,    \
+                                                             static_cast<const TT*>(v), P, H, c, ws.plan,    \
                                                              seq_len, n_splits, ws.part_o, ws.part_ml)
   if (dtype == PP_BF16) {
     if (d == 128) PP_B_LAUNCH(uint16_t, 128);

@@ -61,7 +61,10 @@ struct DocTile {
   static constexpr int CPR = D / 8;                  // 16-byte chunks per row
   static constexpr int TILE_BYTES = NK * ROWB;       // K (or V) tile
   static constexpr int STAGE_BYTES = 2 * TILE_BYTES;
-  static constexpr int NS = 4;                       // LDS ring stages (see the pipeline below)
+#ifndef PP_DOC_STAGES
+#define PP_DOC_STAGES 4
+#endif
+  static constexpr int NS = PP_DOC_STAGES;           // LDS ring stages (see the pipeline below)
   static constexpr int ROWS_PER_KB = 1024 / ROWB;    // rows one wave-wide 16-byte load fills
   static constexpr int NLD = TILE_BYTES / 1024 / NW;  // direct loads per thread per tile (K or V)
   static_assert(NLD >= 1 && TILE_BYTES % (1024 * NW) == 0, "tile shape");
@@ -126,7 +129,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 template <int D, int QB, int NW>
 __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int P,
-    int H, float c, const int32_t* __restrict__ plan_parts, int64_t seq_len, int n_splits,
+    int H, float c, const int32_t* __restrict__ plan, int64_t seq_len, int n_splits,
     float* __restrict__ part_o, float2* __restrict__ part_ml) {
   using TL = DocTile<D, QB, NW>;
   constexpr int NK = TL::NK, NS = TL::NS, NLD = TL::NLD, ROWB = TL::ROWB, CPR = TL::CPR;
@@ -140,7 +143,7 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
   const int split = blockIdx.x, h = blockIdx.y, pt = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int ln = lane & 15, lg = lane >> 4;
-  const int L = doc_prefix_from_parts(plan_parts, seq_len);
+  const int L = load_doc_len(plan);
   const int n_tiles = (L + NK - 1) / NK;
   const int t0 = (int)((int64_t)split * n_tiles / n_splits);
   const int t1 = (int)((int64_t)(split + 1) * n_tiles / n_splits);
@@ -190,7 +193,8 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t ring_base = lds_addr(&ring[0][0]);
   auto issue = [&](int t) {
-    const uint32_t ks = ring_base + ((t - t0) % NS) * TL::STAGE_BYTES;
+    // (wave-uniform; stated so the value stays on the scalar unit for m0)
+    const uint32_t ks = __builtin_amdgcn_readfirstlane(ring_base + ((t - t0) % NS) * TL::STAGE_BYTES);
     const uint32_t vs = ks + TL::TILE_BYTES;
     const int kbase = t * NK;
 #pragma unroll
@@ -338,26 +342,34 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
   };
 
   // ---- pipeline -----------------------------------------------------------------
-  // Tile t is loaded two iterations ahead (ring of NS = 4 stages: tiles t-1
-  // and t are read in iteration t, t+1 and t+2 are in flight).  Waves of
-  // group A (all waves, or the first half when two waves share a SIMD) run
+  // Tile t is loaded NS-2 iterations ahead (tiles t-1 and t are read in
+  // iteration t, t+1 .. t+NS-2 are in flight).  Waves of group A (all waves,
+  // or the first half when two waves share a SIMD) run
   //     [P.V(t-1), QK(t)] (matrix cores) then softmax(t) (vector ALUs);
   // group B runs the same work shifted by half an iteration,
   //     softmax(t-1) then [P.V(t-1), QK(t)],
   // so after each barrier one wave of every SIMD is on the matrix cores while
   // the other is on the vector ALUs.
-  static_assert(NS == 4, "two tiles ahead plus two tiles in use");
+  static_assert(NS >= 3 && NS <= 6, "ring depth");
+  constexpr int AHEAD_T = NS - 2;  // tiles in flight
+  // wait until tile t has landed: at most n later tiles of this wave in flight
+  auto wait_tiles = [&](int n) {
+    if (n <= 0) wait_vmcnt<0>();
+    else if (n == 1) wait_vmcnt<2 * NLD>();
+    else if (n == 2) wait_vmcnt<4 * NLD>();
+    else wait_vmcnt<6 * NLD>();
+  };
   // waves w and w + 4 share a SIMD: alternate groups by (w / 4)
   const bool grp_b = NW >= 8 && ((wave >> 2) & 1);
   if (t0 < t1) {
-    issue(t0);
-    if (t0 + 1 < t1) issue(t0 + 1);
+#pragma unroll
+    for (int i = 0; i < AHEAD_T; ++i)
+      if (t0 + i < t1) issue(t0 + i);
     for (int t = t0; t < t1; ++t) {
-      if (t + 1 < t1) wait_vmcnt<2 * NLD>();  // tile t landed; t+1 may be in flight
-      else wait_vmcnt<0>();
+      wait_tiles(min(AHEAD_T - 1, t1 - 1 - t));  // tile t landed
       __builtin_amdgcn_s_barrier();   // every wave's loads of tile t are in LDS, and every
       asm volatile("" ::: "memory");  // wave is done with tile t-2 (its stage is reused next)
-      if (t + 2 < t1) issue(t + 2);
+      if (t + AHEAD_T < t1) issue(t + AHEAD_T);
       if (!grp_b) {
         if (t > t0) pv(t - 1);
         qk(t);
@@ -398,14 +410,14 @@ constexpr int kF32NK = 32;
 template <int D>
 __global__ __launch_bounds__(kDocThreads) void doc_valu_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v, int P, int H, float c,
-    const int32_t* __restrict__ plan_parts, int64_t seq_len, int n_splits, float* __restrict__ part_o,
+    const int32_t* __restrict__ plan, int64_t seq_len, int n_splits, float* __restrict__ part_o,
     float2* __restrict__ part_ml) {
   __shared__ __attribute__((aligned(16))) float lk[kF32NK][D];
   __shared__ __attribute__((aligned(16))) float lv[kF32NK][D];
   const int split = blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x;
   const int p = blockIdx.z * kDocThreads + tid;
-  const int L = doc_prefix_from_parts(plan_parts, seq_len);
+  const int L = load_doc_len(plan);
   const int n_tiles = (L + kF32NK - 1) / kF32NK;
   const int t0 = (int)((int64_t)split * n_tiles / n_splits);
   const int t1 = (int)((int64_t)(split + 1) * n_tiles / n_splits);
@@ -506,7 +518,7 @@ hipError_t launch_doc(const DocPlan& pl, const void* q, const void* k, const voi
     auto* kk = static_cast<const uint16_t*>(k);
     auto* vv = static_cast<const uint16_t*>(v);
 #define PP_DOC_LAUNCH(DD, QQ, WW)                                                                      \
-  doc_mfma_bf16_kernel<DD, QQ, WW><<<grid, 64 * WW, 0, stream>>>(qq, kk, vv, P, H, c, ws.plan_parts, \
+  doc_mfma_bf16_kernel<DD, QQ, WW><<<grid, 64 * WW, 0, stream>>>(qq, kk, vv, P, H, c, ws.plan, \
                                                                   seq_len, pl.n_splits, ws.part_o, ws.part_ml)
     // dispatch on the exact (d, 16-query blocks per wave, waves) triple
     const int cfg = d * 10000 + pl.qb * 100 + pl.nw;
@@ -525,9 +537,9 @@ hipError_t launch_doc(const DocPlan& pl, const void* q, const void* k, const voi
     auto* kk = static_cast<const float*>(k);
     auto* vv = static_cast<const float*>(v);
     if (d == 128)
-      doc_valu_f32_kernel<128><<<grid, kDocThreads, 0, stream>>>(qq, kk, vv, P, H, c, ws.plan_parts, seq_len, pl.n_splits, ws.part_o, ws.part_ml);
+      doc_valu_f32_kernel<128><<<grid, kDocThreads, 0, stream>>>(qq, kk, vv, P, H, c, ws.plan, seq_len, pl.n_splits, ws.part_o, ws.part_ml);
     else
-      doc_valu_f32_kernel<64><<<grid, kDocThreads, 0, stream>>>(qq, kk, vv, P, H, c, ws.plan_parts, seq_len, pl.n_splits, ws.part_o, ws.part_ml);
+      doc_valu_f32_kernel<64><<<grid, kDocThreads, 0, stream>>>(qq, kk, vv, P, H, c, ws.plan, seq_len, pl.n_splits, ws.part_o, ws.part_ml);
   }
   return hipGetLastError();
 }

@@ -18,30 +18,48 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;
 
 // Workspace layout (byte offsets from a 256-byte aligned base):
-//   [0, 256)              int32 plan_parts[64]: per-chunk first non-document slot
-//   [256, 256 + ML)       float2 part_ml[n_splits][P][H]  (m in log2 units, l)
-//   [..., + O)            float  part_o [n_splits][P][H][d] (unnormalised)
+//   [0, 256)          int32 plan[0] = doc_len (length of the leading id-0 run)
+//   [256, +CNT)       int32 counts[P]: visible slots past the prefix, per stream
+//   [.., +SL)         int32 slots[P][cap]: their ascending slot indices (the
+//                     first cap of them; a stream with more gathers them itself)
+//   [.., +ML)         float2 part_ml[n_splits][P][H]  (m in log2 units, l)
+//   [.., +O)          float  part_o [n_splits][P][H][d] (unnormalised)
 struct Workspace {
-  int32_t* plan_parts;
+  int32_t* plan;
+  int32_t* counts;
+  int32_t* slots;
+  int64_t cap;
   float2* part_ml;
   float* part_o;
 };
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-inline size_t workspace_bytes_for(int n_splits, int64_t P, int64_t H, int64_t d) {
-  size_t ml = align_up((size_t)n_splits * P * H * sizeof(float2), 256);
-  size_t o = align_up((size_t)n_splits * P * H * d * sizeof(float), 256);
-  return 256 /*base alignment slack*/ + 256 /*doc_len*/ + ml + o;
+// Per-stream slot-list capacity kept in the workspace.
+constexpr int64_t kListCapMax = 2048;
+inline int64_t list_cap_for(int64_t seq_len) { return seq_len < kListCapMax ? seq_len : kListCapMax; }
+
+inline size_t workspace_bytes_for(int n_splits, int64_t P, int64_t H, int64_t d, int64_t seq_len) {
+  const size_t cnt = align_up((size_t)P * 4, 256);
+  const size_t sl = align_up((size_t)P * list_cap_for(seq_len) * 4, 256);
+  const size_t ml = align_up((size_t)n_splits * P * H * sizeof(float2), 256);
+  const size_t o = align_up((size_t)n_splits * P * H * d * sizeof(float), 256);
+  return 256 /*base alignment slack*/ + 256 /*plan*/ + cnt + sl + ml + o;
 }
 
-inline Workspace carve_workspace(void* ws, int n_splits, int64_t P, int64_t H) {
-  uintptr_t base = align_up((uintptr_t)ws, 256);
+inline Workspace carve_workspace(void* ws, int n_splits, int64_t P, int64_t H, int64_t seq_len) {
+  uintptr_t at = align_up((uintptr_t)ws, 256);
   Workspace w;
-  w.plan_parts = reinterpret_cast<int32_t*>(base);
-  w.part_ml = reinterpret_cast<float2*>(base + 256);
-  size_t ml = align_up((size_t)n_splits * P * H * sizeof(float2), 256);
-  w.part_o = reinterpret_cast<float*>(base + 256 + ml);
+  w.cap = list_cap_for(seq_len);
+  w.plan = reinterpret_cast<int32_t*>(at);
+  at += 256;
+  w.counts = reinterpret_cast<int32_t*>(at);
+  at += align_up((size_t)P * 4, 256);
+  w.slots = reinterpret_cast<int32_t*>(at);
+  at += align_up((size_t)P * w.cap * 4, 256);
+  w.part_ml = reinterpret_cast<float2*>(at);
+  at += align_up((size_t)n_splits * P * H * sizeof(float2), 256);
+  w.part_o = reinterpret_cast<float*>(at);
   return w;
 }
 
@@ -95,20 +113,10 @@ __device__ __forceinline__ float sum_xor32(float x) {
 }
 
 // ---------------------------------------------------- document prefix ---
-// The plan kernel writes, for each of kPlanWGs workgroups, the first slot
-// with a non-zero id among the chunks it scanned (INT_MAX if none).  The
-// document prefix length is the minimum of those and seq_len; every wave of
-// a consumer computes it from the 64 partials (one load per lane, L2-hot).
-constexpr int kPlanWGs = 64;
-
-__device__ __forceinline__ int doc_prefix_from_parts(const int32_t* __restrict__ parts, int64_t seq_len) {
-  int x = parts[threadIdx.x & 63];
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) x = min(x, __shfl_xor(x, o));
-  // every lane holds the minimum now; make that visible to the compiler so
-  // loops bounded by it stay on the scalar unit
-  x = __builtin_amdgcn_readfirstlane(x);
-  return (int64_t)x < seq_len ? x : (int)seq_len;
+// The plan kernel stores the document prefix length in plan[0]; consumers
+// read it with one (wave-uniform) load.
+__device__ __forceinline__ int load_doc_len(const int32_t* __restrict__ plan) {
+  return __builtin_amdgcn_readfirstlane(plan[0]);
 }
 
 // ------------------------------------------------- visibility compaction ---
@@ -209,13 +217,11 @@ __device__ int collect_visible(const int32_t* __restrict__ sid, int64_t from, in
 // ---------------------------------------------------------- host launchers ---
 // Each returns hipSuccess or the launch error.  All enqueue on `stream`.
 
-// plan_parts[kPlanWGs]: per-workgroup first non-document slot of stream_id[0, seq_len).
-hipError_t launch_plan_doclen(const int32_t* sid, int64_t seq_len, int32_t* plan_parts, hipStream_t stream);
-
-// Integer plan inspection (pp_attn_plan): doc_len, per-stream visible tail
-// counts and slot lists, from the same device code the attention kernels use.
-hipError_t launch_plan_lists(const int32_t* sid, int64_t seq_len, int P, const int32_t* plan_parts,
-                             int32_t* doc_len, int32_t* counts, int32_t* slots, int64_t cap, hipStream_t stream);
+// Visibility plan: doc_len into plan[0]; for every stream s, the number of
+// slots j in [doc_len, seq_len) it sees (counts[s]) and the first cap of
+// them in ascending order (slots[s*cap ...]).  One workgroup per stream.
+hipError_t launch_plan(const int32_t* sid, int64_t seq_len, int P, int32_t* plan, int32_t* counts, int32_t* slots,
+                       int64_t cap, hipStream_t stream);
 
 // Document part, all P queries of a head at once: split-K partial softmax
 // states over [0, doc_len).  Returns the number of splits it will use via

@@ -3,94 +3,139 @@
 // Parallel Prompting packs the shared document first in the request and
 // every stream's question and answer slots after it (project page,
 // illustration: the document and all questions go into one sequence).  The
-// leading run of document slots (id 0) is the part every stream sees; its
-// length is found here on the device, so the host never reads device data.
+// leading run of document slots (id 0) is the part every stream sees and is
+// handled as one dense block; past it, each stream sees only its own slots
+// and any later document slot ("How it works", item 1).  One workgroup per
+// stream finds the prefix length and compacts that stream's visible slots,
+// once per step, for the gather kernel.  Nothing is read back on the host.
 #include "pp_internal.h"
 
 namespace pp {
 namespace {
 
-constexpr int kPlanThreads = 256;
-constexpr int kPlanIds = 16;                              // ids per thread per chunk (4 int4 loads)
-constexpr int64_t kPlanChunk = (int64_t)kPlanThreads * kPlanIds;
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanNW = kPlanThreads / 64;                       // 16 waves: 4 per SIMD hide latency
+constexpr int kPlanG = 8;                                        // granule rows per wave per round
+constexpr int64_t kPlanWaveSpan = (int64_t)64 * kPlanG * 4;      // 2K slots per wave per round
+constexpr int64_t kPlanChunk = kPlanWaveSpan * kPlanNW;          // 32K slots per workgroup per round
 
-// Workgroup b scans chunks b, b + kPlanWGs, ... in increasing order and
-// records the first slot whose id is not 0; it stops at the first chunk that
-// holds one.  Loads are unconditional (clamped granules), one round trip per
-// chunk.
-__global__ __launch_bounds__(kPlanThreads) void plan_doclen_kernel(const int32_t* __restrict__ sid,
-                                                                   int64_t seq_len,
-                                                                   int32_t* __restrict__ parts) {
+// Workgroup = one stream.  In a round wave w owns the 2K slots starting at
+// wb = chunk_base + 2K*w, as 8 rows of 256: lane l, row g holds the int4
+// granule of slots wb + 4*(64g + l) .. +3 (coalesced 1 KB wave-wide loads,
+// all in flight, unconditional at clamped granules).  Per round:
+//   1. while the document prefix is open: the first non-zero id of the
+//      chunk (wave minimum, then workgroup minimum) closes it;
+//   2. the slots j >= doc_len the stream sees (id 0 or s+1) are ranked in
+//      slot order -- within a row by ballots, across rows and waves by
+//      running totals -- and stored at slots[s*cap + rank] (ranks >= cap
+//      are counted only).
+// One global round trip per 32K slots; no atomics decide positions.
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ sid, int64_t seq_len,
+                                                            int32_t* __restrict__ plan, int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ slots, int64_t cap) {
   __shared__ int found;
-  const int tid = threadIdx.x;
+  __shared__ int wsum[kPlanNW];
+  const int s = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int s1 = s + 1;
+  const uint64_t below = (1ull << lane) - 1ull;  // lanes before this one
   if (tid == 0) found = 0x7fffffff;
   __syncthreads();
   const int64_t last_gran = (seq_len - 1) & ~(int64_t)3;
-  for (int64_t cb = (int64_t)blockIdx.x * kPlanChunk; cb < seq_len; cb += kPlanWGs * kPlanChunk) {
-    const int64_t j0 = cb + (int64_t)tid * kPlanIds;
-    int first = 0x7fffffff;
+  int64_t doc_len = -1;  // unknown until a non-zero id is seen
+  int64_t total = 0;
+  for (int64_t cb = 0; cb < seq_len; cb += kPlanChunk) {
+    const int64_t wb = cb + wave * kPlanWaveSpan;  // this wave's first slot
+    int4 x[kPlanG];
 #pragma unroll
-    for (int g = kPlanIds / 4 - 1; g >= 0; --g) {
-      const int64_t jg = j0 + 4 * g;
-      const int4 x = *reinterpret_cast<const int4*>(sid + (jg < last_gran ? jg : last_gran));
-      const int ids[4] = {x.x, x.y, x.z, x.w};
+    for (int g = 0; g < kPlanG; ++g) {
+      const int64_t jg = wb + 4 * (64 * g + lane);
+      x[g] = *reinterpret_cast<const int4*>(sid + (jg < last_gran ? jg : last_gran));
+    }
+    // slot wb + 4*(64g + lane) + e is valid iff 4*(64g + lane) + e < hi
+    const int hi = (int)max<int64_t>(min<int64_t>(seq_len - wb, kPlanWaveSpan), 0);
+    // 1. document prefix
+    if (doc_len < 0) {
+      int first = 0x7fffffff;
 #pragma unroll
-      for (int e = 3; e >= 0; --e) {
-        // bitwise test so every element is read (the load is never split)
-        const unsigned hit = (unsigned)(jg + e < seq_len) & (unsigned)(ids[e] != 0);
-        first = hit ? (int)(jg + e) : first;
+      for (int g = kPlanG - 1; g >= 0; --g) {
+        const int ids[4] = {x[g].x, x[g].y, x[g].z, x[g].w};
+#pragma unroll
+        for (int e = 3; e >= 0; --e) {
+          const int r = 4 * (64 * g + lane) + e;
+          const unsigned hit = (unsigned)(r < hi) & (unsigned)(ids[e] != 0);
+          first = hit ? r : first;
+        }
+      }
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) first = min(first, __shfl_xor(first, o));
+      if (lane == 0 && first != 0x7fffffff) atomicMin(&found, (int)(wb + first));
+      __syncthreads();
+      const int f = found;
+      __syncthreads();  // every thread has read `found` before it can change again
+      if (f != 0x7fffffff) doc_len = f;
+      else if (cb + kPlanChunk >= seq_len) doc_len = seq_len;  // no non-document slot at all
+      if (doc_len < 0) continue;  // the whole chunk is document (uniform)
+    }
+    // 2. visible slots past the prefix, ranked in slot order: r in [lo, hi)
+    const int lo = (int)max<int64_t>(min<int64_t>(doc_len - wb, kPlanWaveSpan), 0);
+    unsigned m[kPlanG];
+    int row_base[kPlanG];
+    int wave_total = 0;
+#pragma unroll
+    for (int g = 0; g < kPlanG; ++g) {
+      const int ids[4] = {x[g].x, x[g].y, x[g].z, x[g].w};
+      m[g] = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * (64 * g + lane) + e;
+        const unsigned vis = (unsigned)(r >= lo) & (unsigned)(r < hi) &
+                             ((unsigned)(ids[e] == 0) | (unsigned)(ids[e] == s1));
+        m[g] |= vis << e;
+      }
+      row_base[g] = wave_total;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) wave_total += __popcll(__builtin_amdgcn_ballot_w64((m[g] >> e) & 1u));
+    }
+    if (lane == 0) wsum[wave] = wave_total;
+    __syncthreads();
+    int before = 0, chunk_total = 0;
+#pragma unroll
+    for (int w = 0; w < kPlanNW; ++w) {
+      const int t = wsum[w];
+      before += w < wave ? t : 0;
+      chunk_total += t;
+    }
+    if (wave_total > 0) {  // uniform
+#pragma unroll
+      for (int g = 0; g < kPlanG; ++g) {
+        // matches of this row in earlier lanes (all four bits), then own bits
+        int rank = row_base[g];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rank += __popcll(__builtin_amdgcn_ballot_w64((m[g] >> e) & 1u) & below);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if ((m[g] >> e) & 1u) {
+            const int64_t pos = total + before + rank;
+            if (pos < cap) slots[(int64_t)s * cap + pos] = (int32_t)(wb + 4 * (64 * g + lane) + e);
+            ++rank;
+          }
+        }
       }
     }
-    if (first != 0x7fffffff) atomicMin(&found, first);
-    __syncthreads();
-    const bool done = found != 0x7fffffff;
-    __syncthreads();  // every thread has read `found` before it can change again
-    if (done) break;
+    total += chunk_total;
+    __syncthreads();  // wsum[] is rewritten next round
   }
-  if (tid == 0) parts[blockIdx.x] = found;
-}
-
-constexpr int kListThreads = 256;
-constexpr int kListScanU = 64;
-constexpr int kListCap = 2048;
-
-// One workgroup per stream: the same ascending compaction the tail kernel
-// runs, written out for inspection.
-__global__ __launch_bounds__(kListThreads) void plan_lists_kernel(const int32_t* __restrict__ sid,
-                                                                  int64_t seq_len,
-                                                                  const int32_t* __restrict__ parts,
-                                                                  int32_t* __restrict__ doc_len_out,
-                                                                  int32_t* __restrict__ counts,
-                                                                  int32_t* __restrict__ slots, int64_t cap) {
-  __shared__ int list[kListCap];
-  __shared__ int scan[kListThreads / 64 + 2];
-  const int s = blockIdx.x;
-  const int doc_len = doc_prefix_from_parts(parts, seq_len);
-  if (s == 0 && threadIdx.x == 0) *doc_len_out = doc_len;
-  int64_t from = doc_len;
-  int64_t total = 0;
-  while (from < seq_len) {
-    int64_t next;
-    const int n = collect_visible<kListThreads, kListScanU>(sid, from, seq_len, s + 1, list, kListCap, &next, scan);
-    for (int i = threadIdx.x; i < n; i += kListThreads)
-      if (total + i < cap) slots[(int64_t)s * cap + total + i] = list[i];
-    total += n;
-    from = next;
-    __syncthreads();  // list[] is refilled by the next round
+  if (tid == 0) {
+    counts[s] = (int32_t)total;
+    if (s == 0) plan[0] = (int32_t)(doc_len < 0 ? seq_len : doc_len);
   }
-  if (threadIdx.x == 0) counts[s] = (int32_t)total;
 }
 
 }  // namespace
 
-hipError_t launch_plan_doclen(const int32_t* sid, int64_t seq_len, int32_t* parts, hipStream_t stream) {
-  plan_doclen_kernel<<<kPlanWGs, kPlanThreads, 0, stream>>>(sid, seq_len, parts);
-  return hipGetLastError();
-}
-
-hipError_t launch_plan_lists(const int32_t* sid, int64_t seq_len, int P, const int32_t* parts, int32_t* doc_len,
-                             int32_t* counts, int32_t* slots, int64_t cap, hipStream_t stream) {
-  plan_lists_kernel<<<P, kListThreads, 0, stream>>>(sid, seq_len, parts, doc_len, counts, slots, cap);
+hipError_t launch_plan(const int32_t* sid, int64_t seq_len, int P, int32_t* plan, int32_t* counts, int32_t* slots,
+                       int64_t cap, hipStream_t stream) {
+  plan_kernel<<<P, kPlanThreads, 0, stream>>>(sid, seq_len, plan, counts, slots, cap);
   return hipGetLastError();
 }
 

@@ -5,16 +5,17 @@
 // Prompting project page, "How it works", item 1).  Instead of testing the
 // stream rule on every slot for every stream -- which makes each stream scan
 // its siblings' answers, the cost the project page's "More results" section
-// blames for the smaller gain on long answers -- each workgroup compacts the
-// slots its own stream sees (ascending, one workgroup-wide scan per 16K-slot
-// chunk) and gathers only those rows.
+// blames for the smaller gain on long answers -- the plan kernel has listed
+// the slots each stream sees (ascending) and this kernel gathers only those
+// rows.  A stream whose list did not fit the plan's capacity compacts it
+// here, in chunks (one workgroup-wide scan per 16K slots).
 //
 // Workgroup = one stream x one group of GW heads (a contiguous GW*d-element
 // slice of every K/V row, so each wave-wide 16-byte load is 1 KB contiguous).
 // Its 4 waves are substreams.  Substream w first merges the document split
 // partial states w, w+4, w+8, ... (written by the document kernel, or by the
 // per-question baseline) -- their loads are issued at kernel start, so they
-// overlap the slot compaction -- then folds in list entries [w*U, w*U + U),
+// overlap the list loads -- then folds in list entries [w*U, w*U + U),
 // [w*U + 4U, ...), ... with an online softmax.  The four states are merged
 // in substream order and the output slice is written.  Every step has a
 // fixed order, so the result is bitwise reproducible.  Splitting streams by
@@ -84,10 +85,12 @@ __device__ __forceinline__ void merge_state(float& M, float& Ls, float* A, float
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(kTailThreads) void tail_merge_kernel(
+// (at most 128 VGPRs: four workgroups per CU)
+__global__ __launch_bounds__(kTailThreads, 4) void tail_merge_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ sid,
-    int64_t seq_len, int P, int H, float c, const int32_t* __restrict__ plan_parts, int n_splits,
-    const float* __restrict__ part_o, const float2* __restrict__ part_ml, T* __restrict__ out) {
+    int64_t seq_len, int P, int H, float c, const int32_t* __restrict__ plan, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ slots, int64_t cap, int n_splits, const float* __restrict__ part_o,
+    const float2* __restrict__ part_ml, T* __restrict__ out) {
   using S = TailShape<T, D>;
   constexpr int VEC = S::VEC, LPH = S::LPH, HPI = S::HPI, GW = S::GW;
   constexpr int RED = kTailNI * (VEC + 2);  // floats per lane in the substream merge
@@ -156,17 +159,15 @@ __global__ __launch_bounds__(kTailThreads) void tail_merge_kernel(
   }
 
   // ---- own slots (and late document slots), gathered ------------------------
-  int64_t from = doc_prefix_from_parts(plan_parts, seq_len);
-  while (from < seq_len) {
-    int64_t next;
-    const int n = collect_visible<kTailThreads, kTailScanU>(sid, from, seq_len, s + 1, list, kTailCap, &next, scan);
+  // fold list entries [0, n) of `lst` into this substream's state
+  auto gather = [&](const int* lst, int n) {
     for (int base = ts * kTailU; base < n; base += kTailNTS * kTailU) {
       // unconditional loads (entries past the end re-read the last one) so
       // that all of them are in flight together
       u32x4 kr[kTailU][kTailNI], vr[kTailU][kTailNI];
 #pragma unroll
       for (int u = 0; u < kTailU; ++u) {
-        const int j = list[min(base + u, n - 1)];
+        const int j = lst[min(base + u, n - 1)];
 #pragma unroll
         for (int i = 0; i < kTailNI; ++i) {
           const int64_t off = (int64_t)j * row + (int64_t)safe_head[i] * D + d0[i];
@@ -197,8 +198,20 @@ __global__ __launch_bounds__(kTailThreads) void tail_merge_kernel(
         }
       }
     }
-    from = next;
-    __syncthreads();  // list[] is refilled by the next round
+  };
+  const int count = counts[s];
+  if (count <= cap) {
+    gather(slots + (int64_t)s * cap, count);  // the plan's list (global, L2-resident)
+  } else {
+    // list longer than the plan kept: compact it here, chunk by chunk
+    int64_t from = load_doc_len(plan);
+    while (from < seq_len) {
+      int64_t next;
+      const int n = collect_visible<kTailThreads, kTailScanU>(sid, from, seq_len, s + 1, list, kTailCap, &next, scan);
+      gather(list, n);
+      from = next;
+      __syncthreads();  // list[] is refilled by the next round
+    }
   }
 
   // ---- merge token substreams (fixed order 0, 1, ..., NTS-1) -----------------
@@ -244,8 +257,8 @@ hipError_t launch_tail_t(int n_splits, const void* q, const void* k, const void*
   using S = TailShape<T, D>;
   const dim3 grid(P, (H + S::GW - 1) / S::GW);
   tail_merge_kernel<T, D><<<grid, kTailThreads, 0, stream>>>(
-      static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), sid, seq_len, P, H, c, ws.plan_parts,
-      n_splits, ws.part_o, ws.part_ml, static_cast<T*>(out));
+      static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), sid, seq_len, P, H, c, ws.plan,
+      ws.counts, ws.slots, ws.cap, n_splits, ws.part_o, ws.part_ml, static_cast<T*>(out));
   return hipGetLastError();
 }
 

@@ -90,6 +90,26 @@ def test_workspace_bytes():
     assert lib.pp_last_error_message() == b""
 
 
+def test_profiled_validation():
+    lib = pp.raw()
+    ev = (ctypes.c_void_p * pp.PP_PROFILE_EVENTS)(*[0x1000 * (i + 1) for i in range(pp.PP_PROFILE_EVENTS)])
+    ws_bytes = lib.pp_attn_workspace_bytes(1000, 8, 4, 128, pp.PP_BF16)
+
+    def call(events, n_events, P=8):
+        return lib.pp_attn_decode_profiled(0, Q, K, V, SID, 1000, P, 4, 128, 0.088, OUT, pp.PP_BF16, WS, ws_bytes,
+                                           None, events, n_events)
+
+    assert call(None, pp.PP_PROFILE_EVENTS) == pp.PP_ERR_INVALID_ARG
+    assert call(ev, pp.PP_PROFILE_EVENTS - 1) == pp.PP_ERR_INVALID_ARG
+    with_null = (ctypes.c_void_p * pp.PP_PROFILE_EVENTS)(*([0x1000] * (pp.PP_PROFILE_EVENTS - 1) + [None]))
+    assert call(with_null, pp.PP_PROFILE_EVENTS) == pp.PP_ERR_INVALID_ARG
+    # the decode arguments are still checked
+    assert call(ev, pp.PP_PROFILE_EVENTS, P=0) == pp.PP_ERR_INVALID_ARG
+    assert len(pp.PROFILE_STAGES) == pp.PP_PROFILE_EVENTS - 1
+    text = open(HEADER).read()
+    assert re.search(r"#define PP_PROFILE_EVENTS %d\b" % pp.PP_PROFILE_EVENTS, text)
+
+
 def test_plan_validation():
     lib = pp.raw()
     n = pp.PP_PLAN_WORKSPACE_BYTES

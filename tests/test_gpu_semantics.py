@@ -57,6 +57,77 @@ def test_bitwise_reproducible(entry):
         assert torch.equal(first.view(torch.int16), again.view(torch.int16))
 
 
+# ---------------------------------------------- concurrency and scheduling ---
+
+def test_profiled_equals_decode():
+    # the profiling variant records events between the same kernels: same bits
+    case = _case(21, P=70, H=8, doc=4100, qmax=40, amax=20)
+    q, k, v, sid = to_gpu(case)
+    say("  gpu: decode vs profiled")
+    a = pp.pp_attn_decode(q, k, v, sid, seq_len=case.seq_len, scale=case.scale)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(pp.PP_PROFILE_EVENTS)]
+    for e in evs:
+        e.record()  # torch creates the underlying hipEvent_t on first record
+    torch.cuda.synchronize()
+    b = pp.pp_attn_decode_profiled([e.cuda_event for e in evs], q, k, v, sid, seq_len=case.seq_len,
+                                   scale=case.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    for i in range(pp.PP_PROFILE_EVENTS - 1):
+        assert evs[i].elapsed_time(evs[i + 1]) >= 0.0
+    assert_close(a, reference(case), what="decode")
+
+
+def test_two_caller_streams():
+    # calls enqueued from two streams, each with its own workspace
+    c1, c2 = _case(22, P=9, doc=2000), _case(23, P=13, H=8, doc=900)
+    g1, g2 = to_gpu(c1), to_gpu(c2)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    say("  gpu: two caller streams")
+    outs = []
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            o1 = pp.pp_attn_decode(*g1, seq_len=c1.seq_len, scale=c1.scale)
+        with torch.cuda.stream(s2):
+            o2 = pp.pp_attn_decode(*g2, seq_len=c2.seq_len, scale=c2.scale)
+        outs.append((o1, o2))
+    torch.cuda.synchronize()
+    r1, r2 = reference(c1), reference(c2)
+    for o1, o2 in outs:
+        assert_close(o1, r1, what="stream 1")
+        assert_close(o2, r2, what="stream 2")
+        assert torch.equal(o1.view(torch.int16), outs[0][0].view(torch.int16))
+        assert torch.equal(o2.view(torch.int16), outs[0][1].view(torch.int16))
+
+
+def test_graph_capture_replays():
+    # a captured step replayed several times, with
+    # eager work and synchronisations between replays; every replay must
+    # equal the eager result
+    case = _case(24, P=33, H=8, doc=3000, qmax=30, amax=20)
+    q, k, v, sid = to_gpu(case)
+    ws = torch.empty(pp.workspace_bytes(case.seq_len, case.P, case.H, case.D, q.dtype), dtype=torch.uint8,
+                     device=q.device)
+    eager = pp.pp_attn_decode(q, k, v, sid, seq_len=case.seq_len, scale=case.scale, workspace=ws).clone()
+    out = torch.zeros_like(q)
+    torch.cuda.synchronize()
+    say("  gpu: capture")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pp.pp_attn_decode(q, k, v, sid, seq_len=case.seq_len, scale=case.scale, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    for i in range(4):
+        say(f"  gpu: replay {i}")
+        out.zero_()
+        ws.fill_(0xFF)  # stale partial states must not matter
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {i}"
+        junk = pp.pp_attn_decode_batched(q, k, v, sid, seq_len=case.seq_len, scale=case.scale)
+        torch.cuda.synchronize()
+        del junk
+
+
 # -------------------------------------------------------- integer plan (a1) ---
 
 def _plan_check(ids_np, seq_len, P, cap=8192):
@@ -118,6 +189,20 @@ def test_late_document_slots_and_foreign_ids(entry):
     sid[torch.from_numpy(pick[9:])] = case.P + 3   # no such stream
     case.stream_id = sid
     assert_close(run(case, entry), reference(case), what="late-doc/foreign ids")
+
+
+@pytest.mark.parametrize("entry", ["decode", "batched"])
+def test_stream_with_more_slots_than_the_plan_lists(entry):
+    # stream 0 sees more slots past the prefix than the plan keeps per stream
+    # (2048): its workgroups compact the list themselves; stream 1 uses the
+    # plan's list; later document slots are in both
+    case = make_case(4, 128, 600, [2500, 10], [600, 12], seed=17, name="long-own-list")
+    rng = np.random.default_rng(18)
+    sid = case.stream_id.clone()
+    pick = rng.choice(np.arange(case.doc_len, case.seq_len), 40, replace=False)
+    sid[torch.from_numpy(pick)] = 0
+    case.stream_id = sid
+    assert_close(run(case, entry), reference(case), what="long own list")
 
 
 @pytest.mark.parametrize("entry", ["decode", "batched"])
