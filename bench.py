@@ -165,6 +165,8 @@ def main():
     ap.add_argument("--workload", default="codellama7b_doc16k_p256")
     ap.add_argument("--seed", type=int, default=1002)
     ap.add_argument("--baseline-steps", type=int, default=5)
+    ap.add_argument("--cold-steps", type=int, default=20,
+                    help="steps timed after a 1 GiB cache-evicting write each (0: skip)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-batched", action="store_true")
@@ -233,7 +235,7 @@ def main():
     # ---- cold steps: 1 GiB written between steps evicts L2 and the MALL -------
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     cold = []
-    for _ in range(min(args.steps, 20)):
+    for _ in range(args.cold_steps):
         flush.fill_(1)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
@@ -243,7 +245,7 @@ def main():
         cold.append(a.elapsed_time(b))
     del flush
     cold.sort()
-    cold_ms = cold[len(cold) // 2]
+    cold_ms = cold[len(cold) // 2] if cold else None
 
     # ---- per-question baseline on the same inputs -----------------------------
     batched = None
