@@ -65,7 +65,8 @@ __global__ __launch_bounds__(kBThreads) void batched_doc_kernel(
   __shared__ float red[NW][VEC + 2][LPK];
 
   const int h = blockIdx.x, split = blockIdx.y, s = blockIdx.z;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // (the wave index is wave-uniform; readfirstlane lets the compiler know)
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int kg = lane / LPK, dl = lane % LPK;
   const int64_t L = load_doc_len(plan);
   const int64_t j_begin = split * L / n_splits, j_end = (split + 1) * L / n_splits;

@@ -26,13 +26,6 @@ namespace {
 
 constexpr int kDocThreads = 256;  // workgroup of the fp32 vector-ALU kernel
 
-// Lazy rescaling threshold (log2 units): the running maximum used as the
-// softmax reference is only raised when a tile's maximum exceeds it by more
-// than this, so exp2(x - m) <= 2^kLazyTau and the O accumulators are rescaled
-// on few tiles.  The final merge uses the same (m, l, O), so the result is
-// unchanged up to rounding.
-constexpr float kLazyTau = 8.0f;
-
 // One direct global->LDS load of 16 bytes per lane (gfx950
 // global_load_lds_dwordx4): lane l's chunk lands at LDS byte lds_base + 16*l.
 // Issued from asm so that the compiler, which cannot tell these LDS writes
@@ -61,10 +54,7 @@ struct DocTile {
   static constexpr int CPR = D / 8;                  // 16-byte chunks per row
   static constexpr int TILE_BYTES = NK * ROWB;       // K (or V) tile
   static constexpr int STAGE_BYTES = 2 * TILE_BYTES;
-#ifndef PP_DOC_STAGES
-#define PP_DOC_STAGES 4
-#endif
-  static constexpr int NS = PP_DOC_STAGES;           // LDS ring stages (see the pipeline below)
+  static constexpr int NS = 4;                       // LDS ring stages (see the pipeline below)
   static constexpr int ROWS_PER_KB = 1024 / ROWB;    // rows one wave-wide 16-byte load fills
   static constexpr int NLD = TILE_BYTES / 1024 / NW;  // direct loads per thread per tile (K or V)
   static_assert(NLD >= 1 && TILE_BYTES % (1024 * NW) == 0, "tile shape");
@@ -238,13 +228,24 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
         for (int qb = 0; qb < QB; ++qb)
           s[qb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kc & 1][kb], qf[qb][kc], s[qb][kb], 0, 0, 0);
     }
+    // the K fragments of chunk 0 first, then per fragment its QB MFMAs and
+    // the read of a fragment one chunk later
+    __builtin_amdgcn_sched_group_barrier(0x100, KB, 0);
+#pragma unroll
+    for (int i = 0; i < KC * KB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
   };
 
   // ---- online softmax of tile t (base 2, lazy rescale) -> packed P^T --------
   uint32_t pb[QB][CH][4];  // P^T as packed bf16 pairs: the P.V B operand
   auto softmax = [&](int t) {
     const int kbase = t * NK;
-    if (kbase + NK > key_end) {  // ragged last tile of the split (uniform)
+    if (__builtin_expect(kbase + NK > key_end, 0)) {  // ragged last tile of the split (uniform)
+      // the empty asm keeps this rare block a branch: without it the compiler
+      // turns the masking into compares and selects run on every tile
+      asm volatile("" ::: "memory");
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -270,7 +271,8 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
       tmax[qb] = smax * cabs;
       grow |= tmax[qb] > m[qb] + kLazyTau;
     }
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform, rare after the first tile
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(grow) != 0, 0)) {  // wave-uniform, rare after the first tile
+      asm volatile("" ::: "memory");  // (kept a branch: no rescale multiplies on other tiles)
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const float mn = fmaxf(m[qb], tmax[qb]);
@@ -338,6 +340,17 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
           lsum[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, __builtin_bit_cast(bf16x8, bw), lsum[qb], 0, 0, 0);
         }
       }
+    }
+    // instruction order for the scheduler: the transposing reads of the
+    // first PV_LEAD steps first, then per step its MFMAs and the reads of a
+    // later step, so LDS latency hides behind PV_LEAD steps of MFMAs
+    constexpr int PV_LEAD = 4;
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * PV_LEAD, 0);
+#pragma unroll
+    for (int i = 0; i < NSTEP; ++i) {
+      if (i % DB == DB - 1) __builtin_amdgcn_sched_group_barrier(0x008, 2 * QB, 0);  // + the row-sum MFMAs
+      else __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
   };
 

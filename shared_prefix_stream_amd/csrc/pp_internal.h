@@ -9,6 +9,13 @@
 
 namespace pp {
 
+// Lazy rescaling threshold (log2 units): the running maximum used as the
+// softmax reference is only raised when a score (or a tile's maximum)
+// exceeds it by more than this, so exp2(x - m) <= 2^kLazyTau and the
+// accumulators are rescaled rarely.  The merges use the same (m, l, O), so
+// the result is unchanged up to rounding.
+constexpr float kLazyTau = 8.0f;
+
 // ----------------------------------------------------------------- types ---
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -21,7 +28,8 @@ constexpr int kWave = 64;
 //   [0, 256)          int32 plan[0] = doc_len (length of the leading id-0 run)
 //   [256, +CNT)       int32 counts[P]: visible slots past the prefix, per stream
 //   [.., +SL)         int32 slots[P][cap]: their ascending slot indices (the
-//                     first cap of them; a stream with more gathers them itself)
+//                     first cap of them; a stream with more gathers them itself;
+//                     cap = min(seq_len, 2048) rounded up to a multiple of 4)
 //   [.., +ML)         float2 part_ml[n_splits][P][H]  (m in log2 units, l)
 //   [.., +O)          float  part_o [n_splits][P][H][d] (unnormalised)
 struct Workspace {
@@ -35,9 +43,13 @@ struct Workspace {
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Per-stream slot-list capacity kept in the workspace.
+// Per-stream slot-list capacity kept in the workspace: a multiple of 4 (the
+// gather kernel reads lists as int4 vectors), at most 2048.
 constexpr int64_t kListCapMax = 2048;
-inline int64_t list_cap_for(int64_t seq_len) { return seq_len < kListCapMax ? seq_len : kListCapMax; }
+inline int64_t list_cap_for(int64_t seq_len) {
+  const int64_t c = seq_len < kListCapMax ? seq_len : kListCapMax;
+  return (c + 3) & ~(int64_t)3;
+}
 
 inline size_t workspace_bytes_for(int n_splits, int64_t P, int64_t H, int64_t d, int64_t seq_len) {
   const size_t cnt = align_up((size_t)P * 4, 256);
@@ -112,6 +124,23 @@ __device__ __forceinline__ float sum_xor32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Sum over aligned groups of G lanes (G in {8, 16, 32, 64}) with DPP lane
+// moves fused into the adds (16-lane rows) and lane swaps across rows: no
+// LDS round trip.  Every lane of a group ends with the group's sum.
+template <int G>
+__device__ __forceinline__ float group_sum_dpp(float v) {
+  static_assert(G == 8 || G == 16 || G == 32 || G == 64, "group size");
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));  // lane ^ 1
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));  // lane ^ 2
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));  // half-row mirror
+  if constexpr (G >= 16)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));  // row mirror
+  if constexpr (G >= 32) v = sum_xor16(v);
+  if constexpr (G >= 64) v = sum_xor32(v);
+  return v;
+}
+
+
 // ---------------------------------------------------- document prefix ---
 // The plan kernel stores the document prefix length in plan[0]; consumers
 // read it with one (wave-uniform) load.
@@ -143,7 +172,7 @@ __device__ int collect_visible(const int32_t* __restrict__ sid, int64_t from, in
   constexpr int G = U / 4;  // int4 granules per thread
   constexpr int NW = NT / 64;
   constexpr int64_t CHUNK = (int64_t)NT * U;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int count = 0;
   int64_t cb = from & ~(int64_t)3;                        // granule-aligned chunk base
   const int64_t last_gran = (seq_len - 1) & ~(int64_t)3;  // last granule holding a slot < seq_len

@@ -35,7 +35,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
                                                             int32_t* __restrict__ slots, int64_t cap) {
   __shared__ int found;
   __shared__ int wsum[kPlanNW];
-  const int s = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int s = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int s1 = s + 1;
   const uint64_t below = (1ull << lane) - 1ull;  // lanes before this one
   if (tid == 0) found = 0x7fffffff;

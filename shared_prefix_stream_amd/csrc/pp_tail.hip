@@ -100,7 +100,8 @@ __global__ __launch_bounds__(kTailThreads, 4) void tail_merge_kernel(
   __shared__ float red[(kTailNTS - 1) * RED * 64];
 
   const int s = blockIdx.x, hg = blockIdx.y;
-  const int tid = threadIdx.x, ts = tid >> 6, lane = tid & 63;
+  // (the substream index is wave-uniform; readfirstlane lets the compiler know)
+  const int tid = threadIdx.x, ts = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int64_t row = (int64_t)H * D;
 
   // lane covers head head[i], dims d0[i] .. +VEC of its 16-byte vector i;
@@ -186,7 +187,7 @@ __global__ __launch_bounds__(kTailThreads, 4) void tail_merge_kernel(
           float dot = 0.f;
 #pragma unroll
           for (int e = 0; e < VEC; ++e) dot = fmaf(qv[i][e], kf[e], dot);
-          dot = group_sum<LPH>(dot);
+          dot = group_sum_dpp<LPH>(dot);
           const float t = dot * c;
           const float mn = fmaxf(mm[i], t);
           const float alpha = fast_exp2(mm[i] - mn);
@@ -199,7 +200,8 @@ __global__ __launch_bounds__(kTailThreads, 4) void tail_merge_kernel(
       }
     }
   };
-  const int count = counts[s];
+  // (wave-uniform: stated so the gather loop's control stays on the scalar unit)
+  const int count = __builtin_amdgcn_readfirstlane(counts[s]);
   if (count <= cap) {
     gather(slots + (int64_t)s * cap, count);  // the plan's list (global, L2-resident)
   } else {
