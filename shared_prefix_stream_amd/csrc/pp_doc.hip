@@ -38,6 +38,12 @@ constexpr int kDocThreads = 256;  // workgroup of the fp32 vector-ALU kernel
 __device__ __forceinline__ void lds_dma16(const void* gaddr, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(gaddr) : "memory", "m0");
 }
+// The same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane
+// byte offset (no 64-bit address arithmetic on the vector ALUs).
+__device__ __forceinline__ void lds_dma16_sv(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -182,19 +188,45 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
   // split's end re-read its last row (finite data, masked out of the scores).
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t ring_base = lds_addr(&ring[0][0]);
+  // Per-lane byte offsets of its 16-byte pieces inside a tile (relative to
+  // the tile's first row of head h), fixed for the whole split; the tile
+  // base is a wave-uniform pointer.  Only the split's ragged last tile
+  // clamps rows (to its last valid row, finite data masked out of the scores).
+  uint32_t koff[NLD], voff[NLD];
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int blk = i * NW + wave_u;
+    const int r = blk * TL::ROWS_PER_KB + lane / CPR;
+    const int slot = lane % CPR;
+    koff[i] = (uint32_t)(((int64_t)r * row + (int64_t)h * D + (slot ^ swz_k<D>(r)) * 8) * 2);
+    voff[i] = (uint32_t)(((int64_t)r * row + (int64_t)h * D + (slot ^ swz_v<D>(r)) * 8) * 2);
+  }
   auto issue = [&](int t) {
     // (wave-uniform; stated so the value stays on the scalar unit for m0)
     const uint32_t ks = __builtin_amdgcn_readfirstlane(ring_base + ((t - t0) % NS) * TL::STAGE_BYTES);
     const uint32_t vs = ks + TL::TILE_BYTES;
     const int kbase = t * NK;
+    const int64_t tile_elems = (int64_t)kbase * row;
+    const uint16_t* kt = k + tile_elems;
+    const uint16_t* vt = v + tile_elems;
+    if (__builtin_expect(kbase + NK <= key_end, 1)) {
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int blk = i * NW + wave_u;
-      const int r = blk * TL::ROWS_PER_KB + lane / CPR;
-      const int slot = lane % CPR;
-      const int64_t g = (int64_t)min(kbase + r, key_end - 1) * row + (int64_t)h * D;
-      lds_dma16(k + g + (slot ^ swz_k<D>(r)) * 8, ks + blk * 1024);
-      lds_dma16(v + g + (slot ^ swz_v<D>(r)) * 8, vs + blk * 1024);
+      for (int i = 0; i < NLD; ++i) {
+        const int blk = i * NW + wave_u;
+        lds_dma16_sv(kt, koff[i], ks + blk * 1024);
+        lds_dma16_sv(vt, voff[i], vs + blk * 1024);
+      }
+    } else {
+      asm volatile("" ::: "memory");  // (the ragged tile: a real branch)
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        const int blk = i * NW + wave_u;
+        const int r = blk * TL::ROWS_PER_KB + lane / CPR;
+        const int slot = lane % CPR;
+        const int64_t g = (int64_t)min(kbase + r, key_end - 1) * row + (int64_t)h * D;
+        lds_dma16(k + g + (slot ^ swz_k<D>(r)) * 8, ks + blk * 1024);
+        lds_dma16(v + g + (slot ^ swz_v<D>(r)) * 8, vs + blk * 1024);
+      }
     }
   };
 
