@@ -19,6 +19,8 @@
 // LDS, never loaded.
 #include <math.h>
 
+#include <type_traits>
+
 #include "pp_internal.h"
 
 namespace pp {
@@ -135,34 +137,56 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
   constexpr int CH = NK / 32;  // P.V contraction steps (32 keys each)
 
   __shared__ __attribute__((aligned(1024))) unsigned char ring[NS][TL::STAGE_BYTES];
+  __shared__ int redo;
 
   const int split = blockIdx.x, h = blockIdx.y, pt = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int ln = lane & 15, lg = lane >> 4;
-  const int L = load_doc_len(plan);
-  const int n_tiles = (L + NK - 1) / NK;
-  const int t0 = (int)((int64_t)split * n_tiles / n_splits);
-  const int t1 = (int)((int64_t)(split + 1) * n_tiles / n_splits);
-  const int key_end = min(t1 * NK, L);
   const int q0 = pt * (16 * QB * NW) + wave * (16 * QB);
   const int64_t row = (int64_t)H * D;  // elements between consecutive slots
 
-  // Scores are taken as x = s * |c| with the sign of c folded into Q (a bf16
-  // sign flip is exact), so the running maximum of x is that of s.
-  const uint32_t qsign = c < 0.f ? 0x80008000u : 0u;
-  const float cabs = fabsf(c);
-
   // Q fragments (B operand of S^T = K Q^T): lane (query ln, group lg) holds
-  // dims kc*32 + 8*lg .. +8 of its query.  Padding queries are zero.
-  bf16x8 qf[QB][KC];
+  // dims kc*32 + 8*lg .. +8 of its query.  Padding queries are zero.  Their
+  // loads are issued first, while the document length is still in flight.
+  u32x4 qw[QB][KC];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int p = q0 + qb * 16 + ln;
+    const int pc = min(p, P - 1);  // in-bounds row for padding lanes (zeroed below)
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+      qw[qb][kc] = *reinterpret_cast<const u32x4*>(q + ((int64_t)pc * H + h) * D + kc * 32 + lg * 8);
+  }
+
+  const int L = load_doc_len(plan);
+  // floor(i * n_tiles / n_splits) as i * (n / k) + i * (n % k) / k: 32-bit
+  // arithmetic only (i <= n_splits <= 256)
+  const uint32_t n_tiles = ((uint32_t)L + NK - 1) / NK;
+  const uint32_t tq = n_tiles / (uint32_t)n_splits, tr = n_tiles % (uint32_t)n_splits;
+  const int t0 = (int)((uint32_t)split * tq + (uint32_t)split * tr / (uint32_t)n_splits);
+  const int t1 = (int)((uint32_t)(split + 1) * tq + (uint32_t)(split + 1) * tr / (uint32_t)n_splits);
+  const int key_end = min(t1 * NK, L);
+
+  // Scores are taken as x = s * |c| with the sign of c folded into Q (a bf16
+  // sign flip is exact), so the running maximum of x is that of s.
+  // Two passes share the pipeline below.
+  //  * Fast pass (always run): p = exp2(x) against the fixed reference 0 --
+  //    no per-tile maximum and no rescaling.  The arithmetic is that of a
+  //    running maximum of 0; it is accurate as long as the row sums stay
+  //    within [2^-64, 2^64] (no overflow of p, no loss to underflow), which
+  //    the pass checks at its end.
+  //  * Exact pass (only if a row sum of the workgroup fell outside): running
+  //    maximum with lazy rescaling, from the start of the split again.
+  const uint32_t qsign = c < 0.f ? 0x80008000u : 0u;
+  const float cabs = fabsf(c);
+
+  bf16x8 qf[QB][KC];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const bool pad = q0 + qb * 16 + ln >= P;
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
-      u32x4 w = u32x4{0u, 0u, 0u, 0u};
-      if (p < P) w = *reinterpret_cast<const u32x4*>(q + ((int64_t)p * H + h) * D + kc * 32 + lg * 8);
-      w ^= qsign;
+      const u32x4 w = pad ? u32x4{0u, 0u, 0u, 0u} : (qw[qb][kc] ^ qsign);
       qf[qb][kc] = __builtin_bit_cast(bf16x8, w);
     }
   }
@@ -201,7 +225,7 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
     koff[i] = (uint32_t)(((int64_t)r * row + (int64_t)h * D + (slot ^ swz_k<D>(r)) * 8) * 2);
     voff[i] = (uint32_t)(((int64_t)r * row + (int64_t)h * D + (slot ^ swz_v<D>(r)) * 8) * 2);
   }
-  auto issue = [&](int t) {
+  auto issue = [&](int t) __attribute__((always_inline)) {
     // (wave-uniform; stated so the value stays on the scalar unit for m0)
     const uint32_t ks = __builtin_amdgcn_readfirstlane(ring_base + ((t - t0) % NS) * TL::STAGE_BYTES);
     const uint32_t vs = ks + TL::TILE_BYTES;
@@ -234,9 +258,9 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
   // The K fragments of dim chunk kc+1 are read from LDS while the MFMAs of
   // chunk kc run (two register buffers), so LDS latency stays hidden.
   f32x4 s[QB][KB];
-  auto qk = [&](int t) {
+  auto qk = [&](int t) __attribute__((always_inline)) {
     const unsigned char* ks = ring[(t - t0) % NS];
-    auto kfrag = [&](int kc, int kb) {
+    auto kfrag = [&](int kc, int kb) __attribute__((always_inline)) {
       const int key = key_of(kb, ln);
       const int col = kc * 4 + lg;
       return *reinterpret_cast<const bf16x8*>(ks + key * ROWB + ((col ^ swz_k<D>(key)) * 16));
@@ -272,7 +296,7 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
 
   // ---- online softmax of tile t (base 2, lazy rescale) -> packed P^T --------
   uint32_t pb[QB][CH][4];  // P^T as packed bf16 pairs: the P.V B operand
-  auto softmax = [&](int t) {
+  auto softmax = [&](int t) __attribute__((always_inline)) {
     const int kbase = t * NK;
     if (__builtin_expect(kbase + NK > key_end, 0)) {  // ragged last tile of the split (uniform)
       // the empty asm keeps this rare block a branch: without it the compiler
@@ -332,12 +356,44 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
     }
   };
 
+  // fast pass: p = exp2(x) with the fixed reference 0
+  auto softmax_fast = [&](int t) __attribute__((always_inline)) {
+    const int kbase = t * NK;
+    if (__builtin_expect(kbase + NK > key_end, 0)) {  // ragged last tile of the split (uniform)
+      asm volatile("" ::: "memory");  // (kept a branch, as in softmax)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = 32 * (kb >> 1) + 8 * lg + 4 * (kb & 1) + i;
+            if (kbase + key >= key_end) s[qb][kb][i] = -INFINITY;
+          }
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int ch = 0; ch < CH; ++ch) {
+        float pv_[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pv_[i] = fast_exp2(s[qb][2 * ch][i] * cabs);
+          pv_[4 + i] = fast_exp2(s[qb][2 * ch + 1][i] * cabs);
+        }
+        pb[qb][ch][0] = pack_bf16x2(pv_[0], pv_[1]);
+        pb[qb][ch][1] = pack_bf16x2(pv_[2], pv_[3]);
+        pb[qb][ch][2] = pack_bf16x2(pv_[4], pv_[5]);
+        pb[qb][ch][3] = pack_bf16x2(pv_[6], pv_[7]);
+      }
+  };
+
   // ---- O^T += V^T P^T for tile t (and the row sums, on the matrix cores) ----
   // V operands are read with the transposing LDS load two (chunk, dim-block)
   // steps ahead of the MFMAs that use them.
-  auto pv = [&](int t) {
+  auto pv = [&](int t) __attribute__((always_inline)) {
     const unsigned char* vs = ring[(t - t0) % NS] + TL::TILE_BYTES;
-    auto vfrag = [&](int ch, int db) {
+    auto vfrag = [&](int ch, int db) __attribute__((always_inline)) {
       // lane (ln, lg) points at row 32ch + 8lg + 4half + ln/4, dims db*16 + 4(ln%4) .. +4
       bf16x4 half2[2];
 #pragma unroll
@@ -398,7 +454,7 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
   static_assert(NS >= 3 && NS <= 6, "ring depth");
   constexpr int AHEAD_T = NS - 2;  // tiles in flight
   // wait until tile t has landed: at most n later tiles of this wave in flight
-  auto wait_tiles = [&](int n) {
+  auto wait_tiles = [&](int n) __attribute__((always_inline)) {
     if (n <= 0) wait_vmcnt<0>();
     else if (n == 1) wait_vmcnt<2 * NLD>();
     else if (n == 2) wait_vmcnt<4 * NLD>();
@@ -406,29 +462,73 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
   };
   // waves w and w + 4 share a SIMD: alternate groups by (w / 4)
   const bool grp_b = NW >= 8 && ((wave >> 2) & 1);
-  if (t0 < t1) {
+  auto pipeline = [&](auto fast_tag) __attribute__((always_inline)) {
+    constexpr bool FAST = decltype(fast_tag)::value;
+    auto smx = [&](int t) __attribute__((always_inline)) {
+      if constexpr (FAST) softmax_fast(t);
+      else softmax(t);
+    };
+    if (t0 < t1) {
 #pragma unroll
-    for (int i = 0; i < AHEAD_T; ++i)
-      if (t0 + i < t1) issue(t0 + i);
-    for (int t = t0; t < t1; ++t) {
-      wait_tiles(min(AHEAD_T - 1, t1 - 1 - t));  // tile t landed
-      __builtin_amdgcn_s_barrier();   // every wave's loads of tile t are in LDS, and every
-      asm volatile("" ::: "memory");  // wave is done with tile t-2 (its stage is reused next)
-      if (t + AHEAD_T < t1) issue(t + AHEAD_T);
-      if (!grp_b) {
-        if (t > t0) pv(t - 1);
-        qk(t);
-        softmax(t);
-      } else {
-        if (t > t0) {
-          softmax(t - 1);
-          pv(t - 1);
+      for (int i = 0; i < AHEAD_T; ++i)
+        if (t0 + i < t1) issue(t0 + i);
+      for (int t = t0; t < t1; ++t) {
+        wait_tiles(min(AHEAD_T - 1, t1 - 1 - t));  // tile t landed
+        __builtin_amdgcn_s_barrier();   // every wave's loads of tile t are in LDS, and every
+        asm volatile("" ::: "memory");  // wave is done with tile t-2 (its stage is reused next)
+        if (t + AHEAD_T < t1) issue(t + AHEAD_T);
+        // A wave on the matrix cores runs at raised priority, so that the
+        // SIMD's arbiter feeds its MFMAs first and the other wave's vector
+        // work fills the issue slots in between.
+        if (!grp_b) {
+          __builtin_amdgcn_s_setprio(1);
+          if (t > t0) pv(t - 1);
+          qk(t);
+          __builtin_amdgcn_s_setprio(0);
+          smx(t);
+        } else {
+          if (t > t0) {
+            smx(t - 1);
+            __builtin_amdgcn_s_setprio(1);
+            pv(t - 1);
+          } else {
+            __builtin_amdgcn_s_setprio(1);
+          }
+          qk(t);
+          __builtin_amdgcn_s_setprio(0);
         }
-        qk(t);
       }
+      if (grp_b) smx(t1 - 1);
+      pv(t1 - 1);
     }
-    if (grp_b) softmax(t1 - 1);
-    pv(t1 - 1);
+  };
+  auto reset_state = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      m[qb] = -INFINITY;
+      lsum[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+
+  pipeline(std::integral_constant<bool, true>{});
+  // every row sum of the workgroup within [2^-64, 2^64] (NaN fails too)?
+  bool bad = false;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float lt = lsum[qb][0];
+    bad |= !(lt >= 0x1p-64f && lt <= 0x1p64f);
+  }
+  const bool wave_bad = t0 < t1 && __builtin_amdgcn_ballot_w64(bad) != 0;  // (all lanes vote)
+  if (lane == 0) redo = 0;
+  __syncthreads();
+  if (wave_bad && lane == 0) atomicOr(&redo, 1);
+  __syncthreads();  // also: every wave is done with the ring
+  const bool exact = __builtin_amdgcn_readfirstlane(redo) != 0;
+  if (exact) {  // workgroup-uniform, rare
+    reset_state();
+    pipeline(std::integral_constant<bool, false>{});
   }
 
   // ---- partial state of this split -------------------------------------------
@@ -438,7 +538,10 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
     const int p = q0 + qb * 16 + ln;
     if (p < P) {
       const int64_t sh = ((int64_t)split * P + p) * H + h;
-      if (lg == 0) part_ml[sh] = make_float2(m[qb], lt);
+      // reference of the split's state: 0 in the fast pass, the running
+      // maximum in the exact pass; an empty split has none (-inf)
+      const float mref = t0 >= t1 ? -INFINITY : (exact ? m[qb] : 0.f);
+      if (lg == 0) part_ml[sh] = make_float2(mref, lt);
 #pragma unroll
       for (int db = 0; db < DB; ++db)
         *reinterpret_cast<f32x4*>(part_o + sh * D + db * 16 + 4 * lg) = o[qb][db];

@@ -2,6 +2,8 @@
 isolation between streams (bit-identical), run-to-run determinism, the
 integer visibility plan (bit-exact vs the oracle), layouts the canonical
 generator does not produce, degenerate cases, and stream semantics."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -241,6 +243,25 @@ def test_p1_is_causal_attention(entry):
 def test_peaked_softmax_outliers(entry):
     case = _case(14, P=8, doc=2000, outlier_frac=0.01, outlier_mult=50.0)
     assert_close(run(case, entry), reference(case), what="outliers")
+
+
+@pytest.mark.parametrize("entry", ["decode", "batched"])
+@pytest.mark.parametrize("kind", ["large_scale", "negative_scale", "all_scores_very_negative", "mixed_splits"])
+def test_extreme_score_ranges(entry, kind):
+    # score ranges whose softmax sums leave [2^-64, 2^64] without a running
+    # maximum: exp2 of the scaled scores overflows, or every term underflows
+    case = _case(16, P=5, doc=3000)
+    if kind == "large_scale":
+        case = dataclasses.replace(case, scale=3.0)
+    elif kind == "negative_scale":
+        case = dataclasses.replace(case, scale=-3.0)
+    elif kind == "all_scores_very_negative":
+        case = dataclasses.replace(case, q=case.q.abs(), k=-case.k.abs(), scale=1.0)
+    else:  # only the document's second half has huge scores (some splits normal, some not)
+        k = case.k.clone()
+        k[1500:case.doc_len] *= 8
+        case = dataclasses.replace(case, k=k, scale=0.4)
+    assert_close(run(case, entry), reference(case), what=kind)
 
 
 # -------------------------------------------------------------- streams ---
