@@ -37,13 +37,23 @@ constexpr int kDocThreads = 256;  // workgroup of the fp32 vector-ALU kernel
 // compiler reserves and does not rely on in this kernel.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
+// The LDS base (and below the global base) is wave-uniform; readfirstlane
+// states it, since a call inside a branch on the wave's group may not be
+// known uniform to the compiler.
 __device__ __forceinline__ void lds_dma16(const void* gaddr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(gaddr) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(__builtin_amdgcn_readfirstlane(lds_base)),
+               "v"(gaddr)
+               : "memory", "m0");
 }
 // The same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane
 // byte offset (no 64-bit address arithmetic on the vector ALUs).
-__device__ __forceinline__ void lds_dma16_sv(const void* sbase, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(voff), "s"(sbase)
+__device__ __forceinline__ void lds_dma16_sv(const void* base, uint32_t voff, uint32_t lds_base) {
+  const uint64_t b = (uint64_t)base;
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  const void* sbase = (const void*)(((uint64_t)hi << 32) | (uint64_t)lo);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(__builtin_amdgcn_readfirstlane(lds_base)),
+               "v"(voff), "s"(sbase)
                : "memory", "m0");
 }
 #pragma clang diagnostic pop
@@ -216,15 +226,22 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
   // the tile's first row of head h), fixed for the whole split; the tile
   // base is a wave-uniform pointer.  Only the split's ragged last tile
   // clamps rows (to its last valid row, finite data masked out of the scores).
-  uint32_t koff[NLD], voff[NLD];
+  // With two waves per SIMD the first wave of each pair issues the loads of
+  // both (the second never waits on the vector-memory counter): the issue
+  // stalls once per SIMD, in the first wave's slack before the barrier,
+  // instead of on every wave right after it.
+  constexpr int NIW = NW >= 8 ? 2 : 1;  // block sets a wave issues: its own (and its SIMD partner's)
+  uint32_t koff[NIW][NLD], voff[NIW][NLD];
 #pragma unroll
-  for (int i = 0; i < NLD; ++i) {
-    const int blk = i * NW + wave_u;
-    const int r = blk * TL::ROWS_PER_KB + lane / CPR;
-    const int slot = lane % CPR;
-    koff[i] = (uint32_t)(((int64_t)r * row + (int64_t)h * D + (slot ^ swz_k<D>(r)) * 8) * 2);
-    voff[i] = (uint32_t)(((int64_t)r * row + (int64_t)h * D + (slot ^ swz_v<D>(r)) * 8) * 2);
-  }
+  for (int sset = 0; sset < NIW; ++sset)
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int blk = i * NW + wave_u + 4 * sset;
+      const int r = blk * TL::ROWS_PER_KB + lane / CPR;
+      const int slot = lane % CPR;
+      koff[sset][i] = (uint32_t)(((int64_t)r * row + (int64_t)h * D + (slot ^ swz_k<D>(r)) * 8) * 2);
+      voff[sset][i] = (uint32_t)(((int64_t)r * row + (int64_t)h * D + (slot ^ swz_v<D>(r)) * 8) * 2);
+    }
   auto issue = [&](int t) __attribute__((always_inline)) {
     // (wave-uniform; stated so the value stays on the scalar unit for m0)
     const uint32_t ks = __builtin_amdgcn_readfirstlane(ring_base + ((t - t0) % NS) * TL::STAGE_BYTES);
@@ -235,22 +252,26 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
     const uint16_t* vt = v + tile_elems;
     if (__builtin_expect(kbase + NK <= key_end, 1)) {
 #pragma unroll
-      for (int i = 0; i < NLD; ++i) {
-        const int blk = i * NW + wave_u;
-        lds_dma16_sv(kt, koff[i], ks + blk * 1024);
-        lds_dma16_sv(vt, voff[i], vs + blk * 1024);
-      }
+      for (int sset = 0; sset < NIW; ++sset)
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+          const int blk = i * NW + wave_u + 4 * sset;
+          lds_dma16_sv(kt, koff[sset][i], ks + blk * 1024);
+          lds_dma16_sv(vt, voff[sset][i], vs + blk * 1024);
+        }
     } else {
       asm volatile("" ::: "memory");  // (the ragged tile: a real branch)
 #pragma unroll
-      for (int i = 0; i < NLD; ++i) {
-        const int blk = i * NW + wave_u;
-        const int r = blk * TL::ROWS_PER_KB + lane / CPR;
-        const int slot = lane % CPR;
-        const int64_t g = (int64_t)min(kbase + r, key_end - 1) * row + (int64_t)h * D;
-        lds_dma16(k + g + (slot ^ swz_k<D>(r)) * 8, ks + blk * 1024);
-        lds_dma16(v + g + (slot ^ swz_v<D>(r)) * 8, vs + blk * 1024);
-      }
+      for (int sset = 0; sset < NIW; ++sset)
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+          const int blk = i * NW + wave_u + 4 * sset;
+          const int r = blk * TL::ROWS_PER_KB + lane / CPR;
+          const int slot = lane % CPR;
+          const int64_t g = (int64_t)min(kbase + r, key_end - 1) * row + (int64_t)h * D;
+          lds_dma16(k + g + (slot ^ swz_k<D>(r)) * 8, ks + blk * 1024);
+          lds_dma16(v + g + (slot ^ swz_v<D>(r)) * 8, vs + blk * 1024);
+        }
     }
   };
 
@@ -443,9 +464,11 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
   };
 
   // ---- pipeline -----------------------------------------------------------------
-  // Tile t is loaded NS-2 iterations ahead (tiles t-1 and t are read in
-  // iteration t, t+1 .. t+NS-2 are in flight).  Waves of group A (all waves,
-  // or the first half when two waves share a SIMD) run
+  // The loads of tile t+NS-2 are issued in iteration t (tiles t-1 and t are
+  // read in iteration t, t+1 .. t+NS-2 are in flight): right after the
+  // barrier with one wave per SIMD, by group A at the end of its part with
+  // two.  Waves of group A (all waves, or the first half when two waves
+  // share a SIMD) run
   //     [P.V(t-1), QK(t)] (matrix cores) then softmax(t) (vector ALUs);
   // group B runs the same work shifted by half an iteration,
   //     softmax(t-1) then [P.V(t-1), QK(t)],
@@ -456,9 +479,9 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
   // wait until tile t has landed: at most n later tiles of this wave in flight
   auto wait_tiles = [&](int n) __attribute__((always_inline)) {
     if (n <= 0) wait_vmcnt<0>();
-    else if (n == 1) wait_vmcnt<2 * NLD>();
-    else if (n == 2) wait_vmcnt<4 * NLD>();
-    else wait_vmcnt<6 * NLD>();
+    else if (n == 1) wait_vmcnt<2 * NLD * NIW>();
+    else if (n == 2) wait_vmcnt<4 * NLD * NIW>();
+    else wait_vmcnt<6 * NLD * NIW>();
   };
   // waves w and w + 4 share a SIMD: alternate groups by (w / 4)
   const bool grp_b = NW >= 8 && ((wave >> 2) & 1);
@@ -469,14 +492,15 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
       else softmax(t);
     };
     if (t0 < t1) {
+      const bool issuer = !grp_b;  // loads are issued (and waited for) by group A only
 #pragma unroll
       for (int i = 0; i < AHEAD_T; ++i)
-        if (t0 + i < t1) issue(t0 + i);
+        if (t0 + i < t1 && issuer) issue(t0 + i);
       for (int t = t0; t < t1; ++t) {
-        wait_tiles(min(AHEAD_T - 1, t1 - 1 - t));  // tile t landed
-        __builtin_amdgcn_s_barrier();   // every wave's loads of tile t are in LDS, and every
-        asm volatile("" ::: "memory");  // wave is done with tile t-2 (its stage is reused next)
-        if (t + AHEAD_T < t1) issue(t + AHEAD_T);
+        if (issuer) wait_tiles(min(AHEAD_T - 1, t1 - 1 - t));  // tile t landed (group A's loads: all of it)
+        __builtin_amdgcn_s_barrier();   // tile t is in LDS, and every wave is done with
+        asm volatile("" ::: "memory");  // tile t-2 (its stage is refilled in this iteration)
+        if (NW < 8 && t + AHEAD_T < t1) issue(t + AHEAD_T);
         // A wave on the matrix cores runs at raised priority, so that the
         // SIMD's arbiter feeds its MFMAs first and the other wave's vector
         // work fills the issue slots in between.
@@ -486,6 +510,7 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
           qk(t);
           __builtin_amdgcn_s_setprio(0);
           smx(t);
+          if (NW >= 8 && t + AHEAD_T < t1) issue(t + AHEAD_T);  // into tile t-2's stage
         } else {
           if (t > t0) {
             smx(t - 1);
