@@ -55,19 +55,21 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     const int hi = (int)max<int64_t>(min<int64_t>(seq_len - wb, kPlanWaveSpan), 0);
     // 1. document prefix
     if (doc_len < 0) {
+      // this wave's first non-zero id: the first row whose ballot is
+      // non-empty, its first lane, then that lane's first element
       int first = 0x7fffffff;
 #pragma unroll
-      for (int g = kPlanG - 1; g >= 0; --g) {
-        const int ids[4] = {x[g].x, x[g].y, x[g].z, x[g].w};
-#pragma unroll
-        for (int e = 3; e >= 0; --e) {
-          const int r = 4 * (64 * g + lane) + e;
-          const unsigned hit = (unsigned)(r < hi) & (unsigned)(ids[e] != 0);
-          first = hit ? r : first;
+      for (int g = 0; g < kPlanG; ++g) {
+        const int r0 = 4 * (64 * g + lane);
+        const unsigned valid = (1u << min(max(hi - r0, 0), 4)) - 1u;
+        const unsigned nz = (((unsigned)(x[g].x != 0)) | ((unsigned)(x[g].y != 0) << 1) |
+                             ((unsigned)(x[g].z != 0) << 2) | ((unsigned)(x[g].w != 0) << 3)) & valid;
+        const uint64_t b = __builtin_amdgcn_ballot_w64(nz != 0);
+        if (first == 0x7fffffff && b != 0) {  // uniform
+          const int l0 = __builtin_ctzll(b);
+          first = 4 * (64 * g + l0) + __builtin_ctz((unsigned)__builtin_amdgcn_readlane((int)nz, l0));
         }
       }
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) first = min(first, __shfl_xor(first, o));
       if (lane == 0 && first != 0x7fffffff) atomicMin(&found, (int)(wb + first));
       __syncthreads();
       const int f = found;
@@ -123,7 +125,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
       }
     }
     total += chunk_total;
-    __syncthreads();  // wsum[] is rewritten next round
+    // wsum[] is rewritten next round (the last round needs no barrier: it
+    // would only wait for this round's stores)
+    if (cb + kPlanChunk < seq_len) __syncthreads();
   }
   if (tid == 0) {
     counts[s] = (int32_t)total;
