@@ -123,6 +123,28 @@ pp_status_t pp_attn_decode_batched(const void* q, const void* k_cache, const voi
                                    int32_t d, float scale, void* out, pp_dtype_t dtype,
                                    void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* pp_attn_decode with a visibility plan computed earlier by pp_attn_plan for
+ * the same stream_id and seq_len, instead of computing it again: a decode
+ * step applies the same stream rule in every layer (Parallel Prompting
+ * project page, "How it works", item 1: the stream id of a KV slot decides
+ * its visibility; the ids do not change between the layers of a step), so
+ * one plan per step serves all of them.
+ *   plan_doc_len   device int32[1], as written by pp_attn_plan
+ *   plan_counts    device int32[P]
+ *   plan_slots     device int32[P * plan_capacity] (NULL if plan_capacity is
+ *                  0); lists longer than plan_capacity are completed on the
+ *                  device from stream_id
+ * The plan buffers are read only and caller-owned; they must not overlap
+ * `out` or the workspace (PP_ERR_INVALID_ARG), and must hold the plan of
+ * this stream_id (a stale plan gives wrong results, it is not detected).
+ * Other arguments, results and errors as pp_attn_decode. */
+pp_status_t pp_attn_decode_planned(const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* stream_id, int64_t seq_len, int32_t P, int32_t H,
+                                   int32_t d, float scale, void* out, pp_dtype_t dtype,
+                                   const int32_t* plan_doc_len, const int32_t* plan_counts,
+                                   const int32_t* plan_slots, int64_t plan_capacity,
+                                   void* workspace, size_t workspace_bytes, void* hip_stream);
+
 /* Profiling variant of pp_attn_decode (batched == 0) or pp_attn_decode_batched
  * (batched != 0): identical arguments, contract and results, and it also
  * records caller-created hipEvent_t events on hip_stream around its kernel

@@ -31,6 +31,7 @@ __all__ = [
     "pp_attn_plan",
     "pp_attn_decode_profiled",
     "PROFILE_STAGES",
+    "pp_attn_decode_planned",
     "PP_OK",
     "PP_ERR_INVALID_ARG",
     "PP_ERR_UNSUPPORTED",
@@ -89,6 +90,9 @@ def _load():
                                             ctypes.POINTER(vp), i32]
     lib.pp_attn_plan.restype = ctypes.c_int
     lib.pp_attn_plan.argtypes = [vp, i64, i32, vp, vp, vp, i64, vp, sz, vp]
+    lib.pp_attn_decode_planned.restype = ctypes.c_int
+    lib.pp_attn_decode_planned.argtypes = [vp, vp, vp, vp, i64, i32, i32, i32, f32, vp, ctypes.c_int, vp, vp, vp, i64,
+                                           vp, sz, vp]
     _lib = lib
     return lib
 
@@ -195,6 +199,32 @@ def pp_attn_decode_batched(q, k_cache, v_cache, stream_id, seq_len: Optional[int
                            scale: Optional[float] = None, out=None, workspace=None):
     """The same step as P independent per-question requests (the baseline)."""
     return _decode("pp_attn_decode_batched", q, k_cache, v_cache, stream_id, seq_len, scale, out, workspace)
+
+
+def pp_attn_decode_planned(q, k_cache, v_cache, stream_id, plan, seq_len: Optional[int] = None,
+                           scale: Optional[float] = None, out=None, workspace=None):
+    """pp_attn_decode with a plan `(doc_len, counts, slots)` returned by
+    pp_attn_plan for the same stream_id and seq_len (one plan per step serves
+    every layer).  `slots` is [P, capacity] (capacity may be 0)."""
+    import torch
+
+    P, H, d, seq_len, scale, code, out, workspace = _prepare(q, k_cache, v_cache, stream_id, seq_len, scale, out,
+                                                             workspace)
+    doc_len, counts, slots = plan
+    for name, t in (("doc_len", doc_len), ("counts", counts), ("slots", slots)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.int32:
+            raise ValueError(f"plan {name} must be an int32 GPU tensor")
+    if doc_len.numel() < 1 or counts.shape != (P,) or slots.dim() != 2 or slots.shape[0] != P:
+        raise ValueError("plan must be (doc_len [1], counts [P], slots [P, capacity])")
+    cap = int(slots.shape[1])
+    if cap > 0 and not slots.is_contiguous():
+        raise ValueError("plan slots must be contiguous")
+    st = _load().pp_attn_decode_planned(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), stream_id.data_ptr(), seq_len, P, H, d, scale,
+        out.data_ptr(), code, doc_len.data_ptr(), counts.data_ptr(), slots.data_ptr() if cap > 0 else None, cap,
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream_handle(q.device))
+    _check(st)
+    return out
 
 
 PP_PROFILE_EVENTS = 4

@@ -88,9 +88,18 @@ size_t required_bytes(int64_t seq_len, int32_t P, int32_t H, int32_t d, pp_dtype
 
 enum class Path { kParallel, kBatched };
 
+// A visibility plan computed earlier by pp_attn_plan (device buffers).
+struct ExternalPlan {
+  const int32_t* doc_len;
+  const int32_t* counts;
+  const int32_t* slots;
+  int64_t capacity;
+};
+
 pp_status_t decode_impl(Path path, const void* q, const void* k, const void* v, const int32_t* sid, int64_t seq_len,
                         int32_t P, int32_t H, int32_t d, float scale, void* out, pp_dtype_t dtype, void* workspace,
-                        size_t workspace_bytes, void* hip_stream, void* const* events = nullptr) {
+                        size_t workspace_bytes, void* hip_stream, void* const* events = nullptr,
+                        const ExternalPlan* xp = nullptr) {
   pp_status_t st = check_shape(seq_len, P, H, d, dtype);
   if (st != PP_OK) return st;
   if (!q || !k || !v || !sid || !out) return fail(PP_ERR_INVALID_ARG, "null q, k_cache, v_cache, stream_id or out");
@@ -105,6 +114,17 @@ pp_status_t decode_impl(Path path, const void* q, const void* k, const void* v, 
   if (overlaps(workspace, workspace_bytes, q, nq) || overlaps(workspace, workspace_bytes, k, nkv) ||
       overlaps(workspace, workspace_bytes, v, nkv) || overlaps(workspace, workspace_bytes, sid, nid))
     return fail(PP_ERR_INVALID_ARG, "workspace overlaps an input");
+  if (xp) {
+    if (!xp->doc_len || !xp->counts) return fail(PP_ERR_INVALID_ARG, "null plan_doc_len or plan_counts");
+    if (xp->capacity < 0 || (xp->capacity > 0 && !xp->slots))
+      return fail(PP_ERR_INVALID_ARG, "plan_slots is null or plan_capacity negative");
+    const size_t ns = (size_t)P * (size_t)xp->capacity * 4;
+    if (overlaps(out, nq, xp->doc_len, 4) || overlaps(out, nq, xp->counts, (size_t)P * 4) ||
+        overlaps(out, nq, xp->slots, ns) || overlaps(workspace, workspace_bytes, xp->doc_len, 4) ||
+        overlaps(workspace, workspace_bytes, xp->counts, (size_t)P * 4) ||
+        overlaps(workspace, workspace_bytes, xp->slots, ns))
+      return fail(PP_ERR_INVALID_ARG, "a plan buffer overlaps out or the workspace");
+  }
   const size_t need = required_bytes(seq_len, P, H, d, dtype);
   if (!workspace || workspace_bytes < need)
     return fail(PP_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : (size_t)0, need);
@@ -115,14 +135,20 @@ pp_status_t decode_impl(Path path, const void* q, const void* k, const void* v, 
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   const float c = (float)((double)scale * 1.4426950408889634074);  // log2(e): softmax in base 2
   const int n_splits = path == Path::kParallel ? pl.doc.n_splits : pl.batched_splits;
-  const pp::Workspace ws = pp::carve_workspace(workspace, n_splits, P, H, seq_len);
+  pp::Workspace ws = pp::carve_workspace(workspace, n_splits, P, H, seq_len);
+  if (xp) {  // the caller's plan (read only) in place of the plan kernel's
+    ws.plan = const_cast<int32_t*>(xp->doc_len);
+    ws.counts = const_cast<int32_t*>(xp->counts);
+    ws.slots = const_cast<int32_t*>(xp->slots);
+    ws.cap = xp->capacity;
+  }
 
   // optional profiling events around the launches
   auto mark = [&](int i) -> hipError_t {
     return events ? hipEventRecord(static_cast<hipEvent_t>(events[i]), stream) : hipSuccess;
   };
   hipError_t e = mark(0);
-  if (e == hipSuccess) e = pp::launch_plan(sid, seq_len, P, ws.plan, ws.counts, ws.slots, ws.cap, stream);
+  if (e == hipSuccess && !xp) e = pp::launch_plan(sid, seq_len, P, ws.plan, ws.counts, ws.slots, ws.cap, stream);
   if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess) {
     e = path == Path::kParallel ? pp::launch_doc(pl.doc, q, k, v, seq_len, P, H, d, dtype, c, ws, stream)
@@ -172,6 +198,16 @@ pp_status_t pp_attn_decode_batched(const void* q, const void* k_cache, const voi
                                    pp_dtype_t dtype, void* workspace, size_t workspace_bytes, void* hip_stream) {
   return decode_impl(Path::kBatched, q, k_cache, v_cache, stream_id, seq_len, P, H, d, scale, out, dtype, workspace,
                      workspace_bytes, hip_stream);
+}
+
+pp_status_t pp_attn_decode_planned(const void* q, const void* k_cache, const void* v_cache, const int32_t* stream_id,
+                                   int64_t seq_len, int32_t P, int32_t H, int32_t d, float scale, void* out,
+                                   pp_dtype_t dtype, const int32_t* plan_doc_len, const int32_t* plan_counts,
+                                   const int32_t* plan_slots, int64_t plan_capacity, void* workspace,
+                                   size_t workspace_bytes, void* hip_stream) {
+  const ExternalPlan xp{plan_doc_len, plan_counts, plan_slots, plan_capacity};
+  return decode_impl(Path::kParallel, q, k_cache, v_cache, stream_id, seq_len, P, H, d, scale, out, dtype, workspace,
+                     workspace_bytes, hip_stream, nullptr, &xp);
 }
 
 pp_status_t pp_attn_decode_profiled(int32_t batched, const void* q, const void* k_cache, const void* v_cache,

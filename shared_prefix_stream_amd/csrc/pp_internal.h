@@ -43,8 +43,8 @@ struct Workspace {
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Per-stream slot-list capacity kept in the workspace: a multiple of 4 (the
-// gather kernel reads lists as int4 vectors), at most 2048.
+// Per-stream slot-list capacity kept in the workspace: at most 2048 (a
+// multiple of 4, so that every list starts 16-byte aligned).
 constexpr int64_t kListCapMax = 2048;
 inline int64_t list_cap_for(int64_t seq_len) {
   const int64_t c = seq_len < kListCapMax ? seq_len : kListCapMax;

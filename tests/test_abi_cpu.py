@@ -26,7 +26,7 @@ def test_library_exports_every_declared_function():
     lib = pp.raw()
     names = _declared_functions()
     assert set(names) >= {"pp_attn_decode", "pp_attn_decode_batched", "pp_attn_workspace_bytes", "pp_attn_plan",
-                          "pp_abi_version", "pp_status_string", "pp_last_error_message"}
+                          "pp_attn_decode_planned", "pp_abi_version", "pp_status_string", "pp_last_error_message"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in ppattn.h but not exported"
 
@@ -123,6 +123,26 @@ def test_plan_validation():
     assert lib.pp_attn_plan(SID + 4, 10, 2, OUT, WS, K, 4, V, n, None) == pp.PP_ERR_INVALID_ARG
     assert lib.pp_attn_plan(SID, 10, 2, OUT, WS, K, 4, None, n, None) == pp.PP_ERR_WORKSPACE
     assert lib.pp_attn_plan(SID, 10, 2, OUT, WS, K, 4, V, 100, None) == pp.PP_ERR_WORKSPACE
+
+
+def test_planned_validation():
+    lib = pp.raw()
+    PD, PC, PS = 0x70000000, 0x80000000, 0x90000000  # fake plan buffers
+    ws_bytes = lib.pp_attn_workspace_bytes(1000, 8, 4, 128, pp.PP_BF16)
+
+    def call(pd=PD, pc=PC, ps=PS, cap=16, P=8, out=OUT, ws=WS, wsb=ws_bytes):
+        return lib.pp_attn_decode_planned(Q, K, V, SID, 1000, P, 4, 128, 0.088, out, pp.PP_BF16, pd, pc, ps, cap, ws,
+                                          wsb, None)
+
+    assert call(pd=None) == pp.PP_ERR_INVALID_ARG
+    assert call(pc=None) == pp.PP_ERR_INVALID_ARG
+    assert call(cap=-1) == pp.PP_ERR_INVALID_ARG
+    assert call(ps=None) == pp.PP_ERR_INVALID_ARG
+    assert call(out=PC + 16) == pp.PP_ERR_INVALID_ARG     # out overlaps the counts
+    assert call(ps=WS + 512) == pp.PP_ERR_INVALID_ARG     # slots overlap the workspace
+    assert call(P=0) == pp.PP_ERR_INVALID_ARG             # the decode arguments are still checked
+    assert call(wsb=1024) == pp.PP_ERR_WORKSPACE
+    assert lib.pp_last_error_message().decode() != ""
 
 
 def test_python_binding_rejects_cpu_tensors():

@@ -264,6 +264,30 @@ def test_extreme_score_ranges(entry, kind):
     assert_close(run(case, entry), reference(case), what=kind)
 
 
+@pytest.mark.parametrize("capacity", ["full", "short", "zero"])
+def test_planned_decode_reuses_one_plan_across_layers(capacity):
+    # one plan for the step's ids, three "layers" with their own q/k/v: the
+    # planned entry gives what pp_attn_decode gives (bitwise), also when the
+    # plan's lists are cut short and completed on the device
+    rng = np.random.default_rng(18)
+    q_lens, a_lens = rng.integers(1, 13, 9).tolist(), rng.integers(0, 9, 9).tolist()
+    layers = [make_case(4, 128, 1300, q_lens, a_lens, seed=18 + i, name=f"layer{i}") for i in range(3)]
+    sid = layers[0].stream_id.to("cuda:0")
+    T, P = layers[0].seq_len, layers[0].P
+    cap = {"full": T, "short": 3, "zero": 0}[capacity]
+    plan = pp.pp_attn_plan(sid, T, P, tail_capacity=cap)
+    torch.cuda.synchronize()
+    if capacity == "short":
+        assert int(plan[1].max()) > cap  # the device-side completion is exercised
+    for case in layers:
+        q, k, v, _ = to_gpu(case)
+        a = pp.pp_attn_decode(q, k, v, sid, seq_len=T, scale=case.scale)
+        b = pp.pp_attn_decode_planned(q, k, v, sid, plan, seq_len=T, scale=case.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), case.name
+        assert_close(b, reference(case), what=case.name)
+
+
 # -------------------------------------------------------------- streams ---
 
 def test_runs_on_a_side_stream_without_host_sync():
