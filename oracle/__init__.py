@@ -7,3 +7,9 @@ from .pp_oracle import (  # noqa: F401
     to_f64,
     visible_slots,
 )
+from .pp_step_oracle import (  # noqa: F401
+    oracle_append_step,
+    rope,
+    round_bf16,
+    shared_positions,
+)
