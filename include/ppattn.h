@@ -93,8 +93,9 @@ const char* pp_status_string(pp_status_t status);
 /* Reason for the calling thread's most recent non-OK status ("" if none). */
 const char* pp_last_error_message(void);
 
-/* Bytes of workspace that pp_attn_decode and pp_attn_decode_batched need for
- * this shape (the larger of the two).  Returns 0 for arguments that either
+/* Bytes of workspace that pp_attn_decode, pp_attn_decode_batched,
+ * pp_attn_decode_planned and pp_attn_decode_append need for this shape (one
+ * size serves all of them).  Returns 0 for arguments that either
  * entry point would reject. */
 size_t pp_attn_workspace_bytes(int64_t seq_len, int32_t P, int32_t H, int32_t d, pp_dtype_t dtype);
 
@@ -144,6 +145,66 @@ pp_status_t pp_attn_decode_planned(const void* q, const void* k_cache, const voi
                                    const int32_t* plan_doc_len, const int32_t* plan_counts,
                                    const int32_t* plan_slots, int64_t plan_capacity,
                                    void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Starts a decode step in which every stream appends one slot (Parallel
+ * Prompting project page, "How it works": each decode step appends one token
+ * per stream and has a fixed shape, so a whole step can be captured once as
+ * a HIP graph and replayed).  The step's start lives in device memory, so
+ * the same launches serve every step:
+ *   base_len       device int32[1]: slots already in the cache; the step's
+ *                  new slots are base_len[0] + s for s in [0, P), and the
+ *                  step's length is seq_len = base_len[0] + P
+ *   stream_id      device int32[max_seq_len]; this call writes
+ *                  stream_id[base_len[0] + s] = s + 1
+ *   plan_head      device int32[2], written: {doc_len, seq_len}
+ *   plan_counts    device int32[P], written: slots past doc_len that stream
+ *                  s sees (including its new one)
+ *   plan_slots     device int32[P * plan_capacity], written: the first
+ *                  plan_capacity of them per stream, ascending (NULL when
+ *                  plan_capacity is 0)
+ * That is pp_attn_plan over the ids with the new slots written.  The
+ * caller advances base_len[0] by P between steps (on the stream, e.g. inside
+ * the captured graph).  A base_len[0] outside [0, max_seq_len - P] writes an
+ * empty plan ({0, 0}, counts 0) and no id; the layers of such a step write
+ * nothing to the caches and zeros to out.  One plan serves every layer of
+ * the step (pp_attn_decode_append).  Buffers are caller-owned device memory
+ * and must not overlap each other, stream_id or base_len
+ * (PP_ERR_INVALID_ARG); stream_id 16-byte aligned.  Errors as above. */
+pp_status_t pp_step_plan(int32_t* stream_id, const int32_t* base_len, int64_t max_seq_len, int32_t P,
+                         int32_t* plan_head, int32_t* plan_counts, int32_t* plan_slots,
+                         int64_t plan_capacity, void* hip_stream);
+
+/* One layer of a decode step started by pp_step_plan: append, then attend.
+ * For every stream s, with seq_len = plan_head[1] and its new slot
+ * j_s = seq_len - P + s:
+ *   pos_s  = plan_head[0] + plan_counts[s] - 1, the shared position of the
+ *            new token: the number of slots stream s sees before it (Parallel
+ *            Prompting project page, "How it works", item 2: every stream's
+ *            positions start right after the document, as if its question
+ *            were the only one)
+ *   rotary embedding at pos_s of q[s] and k_new[s], rotate-half pairs
+ *   (i, i + d/2) turned by pos_s * rope_base^(-2i/d) (rope_base <= 0: no
+ *   rotation), angles in double precision, rotation in fp32, one rounding to
+ *   `dtype`
+ *   k_cache[j_s] = rotated k_new[s];  v_cache[j_s] = v_new[s]
+ *   out = pp_attn_decode_planned(rotated q, k_cache, v_cache, stream_id,
+ *                                seq_len, ...)  with the step's plan.
+ *   q, k_new, v_new  [P, H, d] element type `dtype`, device, read only
+ *   k_cache, v_cache [max_seq_len, H, d], device, rows j_s written
+ *   max_seq_len      host bound of every step's seq_len (sizes the caches,
+ *                    stream_id and the workspace: pp_attn_workspace_bytes(
+ *                    max_seq_len, P, H, d, dtype))
+ * The caches must not overlap each other or any other argument; k_new and
+ * v_new must not overlap out or the workspace (PP_ERR_INVALID_ARG); rope_base
+ * must be finite.  Other arguments, results and errors as
+ * pp_attn_decode_planned. */
+pp_status_t pp_attn_decode_append(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                                  void* v_cache, const int32_t* stream_id, int64_t max_seq_len, int32_t P,
+                                  int32_t H, int32_t d, float scale, double rope_base,
+                                  const int32_t* plan_head, const int32_t* plan_counts,
+                                  const int32_t* plan_slots, int64_t plan_capacity, void* out,
+                                  pp_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                  void* hip_stream);
 
 /* Profiling variant of pp_attn_decode (batched == 0) or pp_attn_decode_batched
  * (batched != 0): identical arguments, contract and results, and it also

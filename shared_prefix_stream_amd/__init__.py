@@ -32,6 +32,8 @@ __all__ = [
     "pp_attn_decode_profiled",
     "PROFILE_STAGES",
     "pp_attn_decode_planned",
+    "pp_step_plan",
+    "pp_attn_decode_append",
     "PP_OK",
     "PP_ERR_INVALID_ARG",
     "PP_ERR_UNSUPPORTED",
@@ -93,6 +95,11 @@ def _load():
     lib.pp_attn_decode_planned.restype = ctypes.c_int
     lib.pp_attn_decode_planned.argtypes = [vp, vp, vp, vp, i64, i32, i32, i32, f32, vp, ctypes.c_int, vp, vp, vp, i64,
                                            vp, sz, vp]
+    lib.pp_step_plan.restype = ctypes.c_int
+    lib.pp_step_plan.argtypes = [vp, vp, i64, i32, vp, vp, vp, i64, vp]
+    lib.pp_attn_decode_append.restype = ctypes.c_int
+    lib.pp_attn_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, f32, ctypes.c_double, vp, vp,
+                                          vp, i64, vp, ctypes.c_int, vp, sz, vp]
     _lib = lib
     return lib
 
@@ -263,3 +270,82 @@ def pp_attn_plan(stream_id, seq_len: int, P: int, tail_capacity: int = 0) -> Tup
                               slots.data_ptr(), int(tail_capacity), ws.data_ptr(), ws.numel(), _stream_handle(dev))
     _check(st)
     return doc_len, counts, slots[:, :tail_capacity]
+
+
+def _gpu_int32(name, t):
+    import torch
+
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.int32 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 GPU tensor")
+
+
+def pp_step_plan(stream_id, base_len, P: int, max_seq_len: Optional[int] = None,
+                 tail_capacity: Optional[int] = None, plan=None) -> Tuple:
+    """Start a decode step that appends one slot per stream at base_len[0] + s
+    (base_len: int32 GPU tensor [1], advanced by the caller between steps).
+    Writes the new ids into stream_id and returns the step's plan
+    (head [2] = {doc_len, seq_len}, counts [P], slots [P, capacity]),
+    written into `plan` when given (e.g. buffers reused by a captured graph)."""
+    import torch
+
+    _gpu_int32("stream_id", stream_id)
+    _gpu_int32("base_len", base_len)
+    if max_seq_len is None:
+        max_seq_len = stream_id.numel()
+    if not (1 <= max_seq_len <= stream_id.numel()):
+        raise ValueError(f"max_seq_len={max_seq_len} must be in [1, len(stream_id)]")
+    dev = stream_id.device
+    if plan is None:
+        if tail_capacity is None:
+            tail_capacity = (min(int(max_seq_len), 2048) + 3) // 4 * 4
+        head = torch.zeros(2, dtype=torch.int32, device=dev)
+        counts = torch.zeros(P, dtype=torch.int32, device=dev)
+        slots = torch.full((P, max(tail_capacity, 1)), -1, dtype=torch.int32, device=dev)[:, :tail_capacity]
+    else:
+        head, counts, slots = plan
+        for name, t in (("head", head), ("counts", counts)):
+            _gpu_int32(f"plan {name}", t)
+        if head.numel() < 2 or counts.shape != (P,) or slots.dim() != 2 or slots.shape[0] != P:
+            raise ValueError("plan must be (head [2], counts [P], slots [P, capacity])")
+        tail_capacity = int(slots.shape[1])
+        if tail_capacity > 0:
+            _gpu_int32("plan slots", slots)
+    _check(_load().pp_step_plan(stream_id.data_ptr(), base_len.data_ptr(), int(max_seq_len), int(P), head.data_ptr(),
+                                counts.data_ptr(), slots.data_ptr() if tail_capacity > 0 else None,
+                                int(tail_capacity), _stream_handle(dev)))
+    return head, counts, slots
+
+
+def pp_attn_decode_append(q, k_new, v_new, k_cache, v_cache, stream_id, plan, scale: Optional[float] = None,
+                          rope_base: float = 10000.0, out=None, workspace=None, max_seq_len: Optional[int] = None):
+    """One layer of a step started by pp_step_plan: the new keys and values
+    go into the caches (keys and queries rotated at the streams' shared
+    positions; rope_base <= 0 switches the rotation off), then the decode
+    attention over the step's seq_len.  Returns `out` without synchronising."""
+    import torch
+
+    if max_seq_len is None:
+        max_seq_len = min(k_cache.shape[0], stream_id.numel()) if k_cache.dim() == 3 else 0
+    P, H, d, max_seq_len, scale, code, out, workspace = _prepare(q, k_cache, v_cache, stream_id, max_seq_len, scale,
+                                                                 out, workspace)
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{name} must be shaped and typed like q")
+    head, counts, slots = plan
+    for name, t in (("head", head), ("counts", counts), ("slots", slots)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.int32:
+            raise ValueError(f"plan {name} must be an int32 GPU tensor")
+    if head.numel() < 2 or counts.shape != (P,) or slots.dim() != 2 or slots.shape[0] != P:
+        raise ValueError("plan must be (head [2], counts [P], slots [P, capacity]) from pp_step_plan")
+    cap = int(slots.shape[1])
+    if cap > 0 and not slots.is_contiguous():
+        raise ValueError("plan slots must be contiguous")
+    st = _load().pp_attn_decode_append(
+        q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        stream_id.data_ptr(), max_seq_len, P, H, d, scale, float(rope_base), head.data_ptr(), counts.data_ptr(),
+        slots.data_ptr() if cap > 0 else None, cap, out.data_ptr(), code, workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream_handle(q.device))
+    _check(st)
+    return out

@@ -96,10 +96,18 @@ struct ExternalPlan {
   int64_t capacity;
 };
 
+// The append part of an appending decode step (the step's new query, key
+// and value per stream, the caches it writes, the rotary base).
+struct AppendArgs {
+  const void* k_new;
+  const void* v_new;
+  double rope_base;
+};
+
 pp_status_t decode_impl(Path path, const void* q, const void* k, const void* v, const int32_t* sid, int64_t seq_len,
                         int32_t P, int32_t H, int32_t d, float scale, void* out, pp_dtype_t dtype, void* workspace,
                         size_t workspace_bytes, void* hip_stream, void* const* events = nullptr,
-                        const ExternalPlan* xp = nullptr) {
+                        const ExternalPlan* xp = nullptr, const AppendArgs* ap = nullptr) {
   pp_status_t st = check_shape(seq_len, P, H, d, dtype);
   if (st != PP_OK) return st;
   if (!q || !k || !v || !sid || !out) return fail(PP_ERR_INVALID_ARG, "null q, k_cache, v_cache, stream_id or out");
@@ -125,6 +133,26 @@ pp_status_t decode_impl(Path path, const void* q, const void* k, const void* v, 
         overlaps(workspace, workspace_bytes, xp->slots, ns))
       return fail(PP_ERR_INVALID_ARG, "a plan buffer overlaps out or the workspace");
   }
+  if (ap) {  // (always with a caller's plan: {doc_len, seq_len}, counts, slots)
+    if (overlaps(out, nq, xp->doc_len, 8) || overlaps(workspace, workspace_bytes, xp->doc_len, 8))
+      return fail(PP_ERR_INVALID_ARG, "a plan buffer overlaps out or the workspace");
+    if (P > seq_len) return fail(PP_ERR_INVALID_ARG, "P=%d exceeds max_seq_len=%lld", P, (long long)seq_len);
+    if (!ap->k_new || !ap->v_new) return fail(PP_ERR_INVALID_ARG, "null k_new or v_new");
+    if (!aligned16(ap->k_new) || !aligned16(ap->v_new))
+      return fail(PP_ERR_INVALID_ARG, "k_new and v_new must be 16-byte aligned");
+    if (!isfinite(ap->rope_base)) return fail(PP_ERR_INVALID_ARG, "rope_base is not finite");
+    // the caches are written: nothing read in the step may share their bytes
+    for (const void* w : {k, v})
+      if (overlaps(w, nkv, q, nq) || overlaps(w, nkv, ap->k_new, nq) || overlaps(w, nkv, ap->v_new, nq) ||
+          overlaps(w, nkv, sid, nid) || overlaps(w, nkv, workspace, workspace_bytes) ||
+          overlaps(w, nkv, xp->doc_len, 8) || overlaps(w, nkv, xp->counts, (size_t)P * 4) ||
+          overlaps(w, nkv, xp->slots, (size_t)P * (size_t)(xp->capacity > 0 ? xp->capacity : 0) * 4))
+        return fail(PP_ERR_INVALID_ARG, "k_cache or v_cache overlaps another argument");
+    if (overlaps(k, nkv, v, nkv)) return fail(PP_ERR_INVALID_ARG, "k_cache and v_cache overlap");
+    if (overlaps(out, nq, ap->k_new, nq) || overlaps(out, nq, ap->v_new, nq) ||
+        overlaps(workspace, workspace_bytes, ap->k_new, nq) || overlaps(workspace, workspace_bytes, ap->v_new, nq))
+      return fail(PP_ERR_INVALID_ARG, "k_new or v_new overlaps out or the workspace");
+  }
   const size_t need = required_bytes(seq_len, P, H, d, dtype);
   if (!workspace || workspace_bytes < need)
     return fail(PP_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : (size_t)0, need);
@@ -135,13 +163,14 @@ pp_status_t decode_impl(Path path, const void* q, const void* k, const void* v, 
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   const float c = (float)((double)scale * 1.4426950408889634074);  // log2(e): softmax in base 2
   const int n_splits = path == Path::kParallel ? pl.doc.n_splits : pl.batched_splits;
-  pp::Workspace ws = pp::carve_workspace(workspace, n_splits, P, H, seq_len);
+  pp::Workspace ws = pp::carve_workspace(workspace, n_splits, P, H, d, seq_len);
   if (xp) {  // the caller's plan (read only) in place of the plan kernel's
     ws.plan = const_cast<int32_t*>(xp->doc_len);
     ws.counts = const_cast<int32_t*>(xp->counts);
     ws.slots = const_cast<int32_t*>(xp->slots);
     ws.cap = xp->capacity;
   }
+  if (ap) ws.dyn_len = xp->doc_len + 1;  // {doc_len, seq_len} of the step
 
   // optional profiling events around the launches
   auto mark = [&](int i) -> hipError_t {
@@ -149,6 +178,11 @@ pp_status_t decode_impl(Path path, const void* q, const void* k, const void* v, 
   };
   hipError_t e = mark(0);
   if (e == hipSuccess && !xp) e = pp::launch_plan(sid, seq_len, P, ws.plan, ws.counts, ws.slots, ws.cap, stream);
+  if (e == hipSuccess && ap) {  // new keys and values into the caches, rotated queries into the workspace
+    e = pp::launch_append_rope(q, ap->k_new, ap->v_new, const_cast<void*>(k), const_cast<void*>(v), P, H, d, dtype,
+                               ap->rope_base, ws.plan, ws.counts, seq_len, ws.q_rot, stream);
+    q = ws.q_rot;
+  }
   if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess) {
     e = path == Path::kParallel ? pp::launch_doc(pl.doc, q, k, v, seq_len, P, H, d, dtype, c, ws, stream)
@@ -208,6 +242,44 @@ pp_status_t pp_attn_decode_planned(const void* q, const void* k_cache, const voi
   const ExternalPlan xp{plan_doc_len, plan_counts, plan_slots, plan_capacity};
   return decode_impl(Path::kParallel, q, k_cache, v_cache, stream_id, seq_len, P, H, d, scale, out, dtype, workspace,
                      workspace_bytes, hip_stream, nullptr, &xp);
+}
+
+pp_status_t pp_step_plan(int32_t* stream_id, const int32_t* base_len, int64_t max_seq_len, int32_t P,
+                         int32_t* plan_head, int32_t* plan_counts, int32_t* plan_slots, int64_t plan_capacity,
+                         void* hip_stream) {
+  if (max_seq_len < 1 || max_seq_len > PP_MAX_SEQ_LEN)
+    return fail(PP_ERR_INVALID_ARG, "max_seq_len=%lld out of range", (long long)max_seq_len);
+  if (P < 1 || P > PP_MAX_STREAMS || P > max_seq_len)
+    return fail(PP_ERR_INVALID_ARG, "P=%d out of range [1, min(%d, max_seq_len)]", P, PP_MAX_STREAMS);
+  if (!stream_id || !base_len || !plan_head || !plan_counts) return fail(PP_ERR_INVALID_ARG, "null pointer");
+  if (plan_capacity < 0 || (plan_capacity > 0 && !plan_slots))
+    return fail(PP_ERR_INVALID_ARG, "plan_slots is null or plan_capacity negative");
+  if (!aligned16(stream_id)) return fail(PP_ERR_INVALID_ARG, "stream_id must be 16-byte aligned");
+  const size_t nid = (size_t)max_seq_len * 4, nc = (size_t)P * 4, ns = (size_t)P * (size_t)plan_capacity * 4;
+  const void* outs[3] = {plan_head, plan_counts, plan_slots};
+  const size_t nout[3] = {8, nc, ns};
+  for (int i = 0; i < 3; ++i) {
+    if (overlaps(outs[i], nout[i], stream_id, nid) || overlaps(outs[i], nout[i], base_len, 4))
+      return fail(PP_ERR_INVALID_ARG, "a plan buffer overlaps stream_id or base_len");
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(outs[i], nout[i], outs[j], nout[j])) return fail(PP_ERR_INVALID_ARG, "plan buffers overlap");
+  }
+  if (overlaps(base_len, 4, stream_id, nid)) return fail(PP_ERR_INVALID_ARG, "base_len overlaps stream_id");
+  hipError_t e = pp::launch_plan_append(stream_id, base_len, max_seq_len, P, plan_head, plan_counts, plan_slots,
+                                        plan_capacity, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(PP_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+pp_status_t pp_attn_decode_append(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                                  const int32_t* stream_id, int64_t max_seq_len, int32_t P, int32_t H, int32_t d,
+                                  float scale, double rope_base, const int32_t* plan_head, const int32_t* plan_counts,
+                                  const int32_t* plan_slots, int64_t plan_capacity, void* out, pp_dtype_t dtype,
+                                  void* workspace, size_t workspace_bytes, void* hip_stream) {
+  const ExternalPlan xp{plan_head, plan_counts, plan_slots, plan_capacity};
+  const AppendArgs ap{k_new, v_new, rope_base};
+  return decode_impl(Path::kParallel, q, k_cache, v_cache, stream_id, max_seq_len, P, H, d, scale, out, dtype,
+                     workspace, workspace_bytes, hip_stream, nullptr, &xp, &ap);
 }
 
 pp_status_t pp_attn_decode_profiled(int32_t batched, const void* q, const void* k_cache, const void* v_cache,

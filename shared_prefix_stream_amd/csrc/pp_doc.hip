@@ -168,7 +168,7 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
       qw[qb][kc] = *reinterpret_cast<const u32x4*>(q + ((int64_t)pc * H + h) * D + kc * 32 + lg * 8);
   }
 
-  const int L = load_doc_len(plan);
+  const int L = (int)min<int64_t>(load_doc_len(plan), seq_len);  // a plan never exceeds the slots given
   // floor(i * n_tiles / n_splits) as i * (n / k) + i * (n % k) / k: 32-bit
   // arithmetic only (i <= n_splits <= 256)
   const uint32_t n_tiles = ((uint32_t)L + NK - 1) / NK;
@@ -590,7 +590,7 @@ __global__ __launch_bounds__(kDocThreads) void doc_valu_f32_kernel(
   const int split = blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x;
   const int p = blockIdx.z * kDocThreads + tid;
-  const int L = load_doc_len(plan);
+  const int L = (int)min<int64_t>(load_doc_len(plan), seq_len);  // a plan never exceeds the slots given
   const int n_tiles = (L + kF32NK - 1) / kF32NK;
   const int t0 = (int)((int64_t)split * n_tiles / n_splits);
   const int t1 = (int)((int64_t)(split + 1) * n_tiles / n_splits);

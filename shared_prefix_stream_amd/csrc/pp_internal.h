@@ -32,6 +32,8 @@ constexpr int kWave = 64;
 //                     cap = min(seq_len, 2048) rounded up to a multiple of 4)
 //   [.., +ML)         float2 part_ml[n_splits][P][H]  (m in log2 units, l)
 //   [.., +O)          float  part_o [n_splits][P][H][d] (unnormalised)
+//   [.., +QR)         the step's rotated queries [P][H][d] (appending step
+//                     only; room for 4-byte elements)
 struct Workspace {
   int32_t* plan;
   int32_t* counts;
@@ -39,6 +41,10 @@ struct Workspace {
   int64_t cap;
   float2* part_ml;
   float* part_o;
+  void* q_rot;
+  // appending step: the step's length lives on the device (plan[1]); the
+  // host-side seq_len is then only an upper bound
+  const int32_t* dyn_len = nullptr;
 };
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -56,10 +62,11 @@ inline size_t workspace_bytes_for(int n_splits, int64_t P, int64_t H, int64_t d,
   const size_t sl = align_up((size_t)P * list_cap_for(seq_len) * 4, 256);
   const size_t ml = align_up((size_t)n_splits * P * H * sizeof(float2), 256);
   const size_t o = align_up((size_t)n_splits * P * H * d * sizeof(float), 256);
-  return 256 /*base alignment slack*/ + 256 /*plan*/ + cnt + sl + ml + o;
+  const size_t qr = align_up((size_t)P * H * d * 4, 256);
+  return 256 /*base alignment slack*/ + 256 /*plan*/ + cnt + sl + ml + o + qr;
 }
 
-inline Workspace carve_workspace(void* ws, int n_splits, int64_t P, int64_t H, int64_t seq_len) {
+inline Workspace carve_workspace(void* ws, int n_splits, int64_t P, int64_t H, int64_t d, int64_t seq_len) {
   uintptr_t at = align_up((uintptr_t)ws, 256);
   Workspace w;
   w.cap = list_cap_for(seq_len);
@@ -72,6 +79,8 @@ inline Workspace carve_workspace(void* ws, int n_splits, int64_t P, int64_t H, i
   w.part_ml = reinterpret_cast<float2*>(at);
   at += align_up((size_t)n_splits * P * H * sizeof(float2), 256);
   w.part_o = reinterpret_cast<float*>(at);
+  at += align_up((size_t)n_splits * P * H * d * sizeof(float), 256);
+  w.q_rot = reinterpret_cast<void*>(at);
   return w;
 }
 
@@ -251,6 +260,22 @@ __device__ int collect_visible(const int32_t* __restrict__ sid, int64_t from, in
 // them in ascending order (slots[s*cap ...]).  One workgroup per stream.
 hipError_t launch_plan(const int32_t* sid, int64_t seq_len, int P, int32_t* plan, int32_t* counts, int32_t* slots,
                        int64_t cap, hipStream_t stream);
+
+// The same for a decode step that appends one slot per stream: the step
+// starts at *base_len (device), stream s's new slot is *base_len + s and gets
+// id s + 1 (written here), the plan covers seq_len = *base_len + P and
+// plan[1] = seq_len.  max_len bounds seq_len; a base past it gives an empty
+// plan.
+hipError_t launch_plan_append(int32_t* sid, const int32_t* base_len, int64_t max_len, int P, int32_t* plan,
+                              int32_t* counts, int32_t* slots, int64_t cap, hipStream_t stream);
+
+// Rotary embedding of the step's new queries and keys at their shared
+// positions (from the plan), and the new keys and values written to the
+// cache slots [seq_len - P, seq_len); the rotated queries go to q_rot.
+// rope_base <= 0: no rotation.
+hipError_t launch_append_rope(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                              int P, int H, int d, pp_dtype_t dtype, double rope_base, const int32_t* plan,
+                              const int32_t* counts, int64_t max_len, void* q_rot, hipStream_t stream);
 
 // Document part, all P queries of a head at once: split-K partial softmax
 // states over [0, doc_len).  Returns the number of splits it will use via

@@ -30,14 +30,38 @@ constexpr int64_t kPlanChunk = kPlanWaveSpan * kPlanNW;          // 32K slots pe
 //      running totals -- and stored at slots[s*cap + rank] (ranks >= cap
 //      are counted only).
 // One global round trip per 32K slots; no atomics decide positions.
+//
+// APPEND (a decode step that appends one slot per stream): the step starts
+// at base = *base_len, stream s's new slot is base + s, and the plan covers
+// seq_len = base + P, where the `seq_len` argument is only the largest
+// allowed length.  The ids of [base, base + P) are taken as s + 1 whatever
+// memory holds (other workgroups may be writing them), workgroup s stores
+// its own, and plan[1] = seq_len.  A base outside [0, limit - P] gives an
+// empty plan (plan[0] = plan[1] = 0, no counts, nothing written).
+template <bool APPEND>
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ sid, int64_t seq_len,
                                                             int32_t* __restrict__ plan, int32_t* __restrict__ counts,
-                                                            int32_t* __restrict__ slots, int64_t cap) {
+                                                            int32_t* __restrict__ slots, int64_t cap,
+                                                            int32_t* sid_out, const int32_t* base_len) {
   __shared__ int found;
   __shared__ int wsum[kPlanNW];
   const int s = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int s1 = s + 1;
   const uint64_t below = (1ull << lane) - 1ull;  // lanes before this one
+  int64_t app = seq_len;  // first appended slot
+  if constexpr (APPEND) {
+    const int64_t b = __builtin_amdgcn_readfirstlane(base_len[0]);
+    const int64_t P = gridDim.x;
+    if (b < 0 || b > seq_len - P) {
+      if (tid == 0) {
+        counts[s] = 0;
+        if (s == 0) plan[0] = plan[1] = 0;
+      }
+      return;
+    }
+    app = b;
+    seq_len = b + P;
+  }
   if (tid == 0) found = 0x7fffffff;
   __syncthreads();
   const int64_t last_gran = (seq_len - 1) & ~(int64_t)3;
@@ -49,7 +73,14 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
 #pragma unroll
     for (int g = 0; g < kPlanG; ++g) {
       const int64_t jg = wb + 4 * (64 * g + lane);
-      x[g] = *reinterpret_cast<const int4*>(sid + (jg < last_gran ? jg : last_gran));
+      const int64_t jl = jg < last_gran ? jg : last_gran;
+      x[g] = *reinterpret_cast<const int4*>(sid + jl);
+      if constexpr (APPEND) {
+        x[g].x = jl >= app ? (int)(jl - app) + 1 : x[g].x;
+        x[g].y = jl + 1 >= app ? (int)(jl + 1 - app) + 1 : x[g].y;
+        x[g].z = jl + 2 >= app ? (int)(jl + 2 - app) + 1 : x[g].z;
+        x[g].w = jl + 3 >= app ? (int)(jl + 3 - app) + 1 : x[g].w;
+      }
     }
     // slot wb + 4*(64g + lane) + e is valid iff 4*(64g + lane) + e < hi
     const int hi = (int)max<int64_t>(min<int64_t>(seq_len - wb, kPlanWaveSpan), 0);
@@ -132,6 +163,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
   if (tid == 0) {
     counts[s] = (int32_t)total;
     if (s == 0) plan[0] = (int32_t)(doc_len < 0 ? seq_len : doc_len);
+    if constexpr (APPEND) {
+      sid_out[app + s] = s1;
+      if (s == 0) plan[1] = (int32_t)seq_len;
+    }
   }
 }
 
@@ -139,7 +174,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
 
 hipError_t launch_plan(const int32_t* sid, int64_t seq_len, int P, int32_t* plan, int32_t* counts, int32_t* slots,
                        int64_t cap, hipStream_t stream) {
-  plan_kernel<<<P, kPlanThreads, 0, stream>>>(sid, seq_len, plan, counts, slots, cap);
+  plan_kernel<false><<<P, kPlanThreads, 0, stream>>>(sid, seq_len, plan, counts, slots, cap, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_plan_append(int32_t* sid, const int32_t* base_len, int64_t max_len, int P, int32_t* plan,
+                              int32_t* counts, int32_t* slots, int64_t cap, hipStream_t stream) {
+  plan_kernel<true><<<P, kPlanThreads, 0, stream>>>(sid, max_len, plan, counts, slots, cap, sid, base_len);
   return hipGetLastError();
 }
 

@@ -90,7 +90,7 @@ __global__ __launch_bounds__(kTailThreads, 4) void tail_merge_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ sid,
     int64_t seq_len, int P, int H, float c, const int32_t* __restrict__ plan, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ slots, int64_t cap, int n_splits, const float* __restrict__ part_o,
-    const float2* __restrict__ part_ml, T* __restrict__ out) {
+    const float2* __restrict__ part_ml, T* __restrict__ out, const int32_t* __restrict__ dyn_len) {
   using S = TailShape<T, D>;
   constexpr int VEC = S::VEC, LPH = S::LPH, HPI = S::HPI, GW = S::GW;
   constexpr int RED = kTailNI * (VEC + 2);  // floats per lane in the substream merge
@@ -206,10 +206,12 @@ __global__ __launch_bounds__(kTailThreads, 4) void tail_merge_kernel(
     gather(slots + (int64_t)s * cap, count);  // the plan's list (global, L2-resident)
   } else {
     // list longer than the plan kept: compact it here, chunk by chunk
+    // (an appending step's length is on the device; seq_len bounds it)
+    const int64_t len = dyn_len ? min<int64_t>(__builtin_amdgcn_readfirstlane(dyn_len[0]), seq_len) : seq_len;
     int64_t from = load_doc_len(plan);
-    while (from < seq_len) {
+    while (from < len) {
       int64_t next;
-      const int n = collect_visible<kTailThreads, kTailScanU>(sid, from, seq_len, s + 1, list, kTailCap, &next, scan);
+      const int n = collect_visible<kTailThreads, kTailScanU>(sid, from, len, s + 1, list, kTailCap, &next, scan);
       gather(list, n);
       from = next;
       __syncthreads();  // list[] is refilled by the next round
@@ -260,7 +262,7 @@ hipError_t launch_tail_t(int n_splits, const void* q, const void* k, const void*
   const dim3 grid(P, (H + S::GW - 1) / S::GW);
   tail_merge_kernel<T, D><<<grid, kTailThreads, 0, stream>>>(
       static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), sid, seq_len, P, H, c, ws.plan,
-      ws.counts, ws.slots, ws.cap, n_splits, ws.part_o, ws.part_ml, static_cast<T*>(out));
+      ws.counts, ws.slots, ws.cap, n_splits, ws.part_o, ws.part_ml, static_cast<T*>(out), ws.dyn_len);
   return hipGetLastError();
 }
 

@@ -26,7 +26,8 @@ def test_library_exports_every_declared_function():
     lib = pp.raw()
     names = _declared_functions()
     assert set(names) >= {"pp_attn_decode", "pp_attn_decode_batched", "pp_attn_workspace_bytes", "pp_attn_plan",
-                          "pp_attn_decode_planned", "pp_abi_version", "pp_status_string", "pp_last_error_message"}
+                          "pp_attn_decode_planned", "pp_step_plan", "pp_attn_decode_append",
+                          "pp_abi_version", "pp_status_string", "pp_last_error_message"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in ppattn.h but not exported"
 
@@ -141,6 +142,55 @@ def test_planned_validation():
     assert call(out=PC + 16) == pp.PP_ERR_INVALID_ARG     # out overlaps the counts
     assert call(ps=WS + 512) == pp.PP_ERR_INVALID_ARG     # slots overlap the workspace
     assert call(P=0) == pp.PP_ERR_INVALID_ARG             # the decode arguments are still checked
+    assert call(wsb=1024) == pp.PP_ERR_WORKSPACE
+    assert lib.pp_last_error_message().decode() != ""
+
+
+def test_step_plan_validation():
+    lib = pp.raw()
+    BASE, HEAD, CNT, SL = 0x60000000, 0x70000000, 0x80000000, 0x90000000
+
+    def call(sid=SID, base=BASE, max_len=1000, P=8, head=HEAD, cnt=CNT, sl=SL, cap=16):
+        return lib.pp_step_plan(sid, base, max_len, P, head, cnt, sl, cap, None)
+
+    assert call(sid=None) == pp.PP_ERR_INVALID_ARG
+    assert call(base=None) == pp.PP_ERR_INVALID_ARG
+    assert call(head=None) == pp.PP_ERR_INVALID_ARG
+    assert call(cnt=None) == pp.PP_ERR_INVALID_ARG
+    assert call(sl=None) == pp.PP_ERR_INVALID_ARG             # capacity > 0 needs slots
+    assert call(cap=-1) == pp.PP_ERR_INVALID_ARG
+    assert call(P=0) == pp.PP_ERR_INVALID_ARG
+    assert call(max_len=7) == pp.PP_ERR_INVALID_ARG            # P > max_seq_len
+    assert call(max_len=0) == pp.PP_ERR_INVALID_ARG
+    assert call(sid=SID + 4) == pp.PP_ERR_INVALID_ARG          # misaligned ids
+    assert call(head=SID + 400) == pp.PP_ERR_INVALID_ARG       # written over the ids
+    assert call(base=SID + 3996) == pp.PP_ERR_INVALID_ARG      # base inside the ids
+    assert call(cnt=SL + 64) == pp.PP_ERR_INVALID_ARG          # plan buffers overlap
+    assert lib.pp_last_error_message().decode() != ""
+
+
+def test_decode_append_validation():
+    lib = pp.raw()
+    KN, VN, HEAD, CNT, SL = 0x70000000, 0x78000000, 0x80000000, 0x90000000, 0xA0000000
+    ws_bytes = lib.pp_attn_workspace_bytes(1000, 8, 4, 128, pp.PP_BF16)
+
+    def call(q=Q, kn=KN, vn=VN, k=K, v=V, max_len=1000, P=8, rope=1e4, out=OUT, head=HEAD, ws=WS, wsb=ws_bytes):
+        return lib.pp_attn_decode_append(q, kn, vn, k, v, SID, max_len, P, 4, 128, 0.088, rope, head, CNT, SL, 16, out,
+                                         pp.PP_BF16, ws, wsb, None)
+
+    assert call(kn=None) == pp.PP_ERR_INVALID_ARG
+    assert call(vn=VN + 8) == pp.PP_ERR_INVALID_ARG            # misaligned
+    assert call(rope=float("inf")) == pp.PP_ERR_INVALID_ARG
+    assert call(head=None) == pp.PP_ERR_INVALID_ARG
+    assert call(q=K + 4096) == pp.PP_ERR_INVALID_ARG           # the written cache holds q
+    assert call(kn=V + 1024) == pp.PP_ERR_INVALID_ARG          # ... or a new key
+    assert call(v=K + 1000 * 4 * 128 * 2 - 256) == pp.PP_ERR_INVALID_ARG  # the caches overlap
+    assert call(head=K + 64) == pp.PP_ERR_INVALID_ARG          # the plan lives in a cache
+    assert call(head=OUT + 4) == pp.PP_ERR_INVALID_ARG         # plan head (8 bytes) overlaps out
+    assert call(kn=OUT) == pp.PP_ERR_INVALID_ARG
+    assert call(vn=WS + 4096) == pp.PP_ERR_INVALID_ARG
+    assert call(P=0) == pp.PP_ERR_INVALID_ARG
+    assert call(max_len=6, wsb=1 << 30) == pp.PP_ERR_INVALID_ARG  # P > max_seq_len
     assert call(wsb=1024) == pp.PP_ERR_WORKSPACE
     assert lib.pp_last_error_message().decode() != ""
 
