@@ -157,6 +157,78 @@ def copy_calibration(steps: int):
                       "gbs_read_plus_write": 2 * n / ms / 1e6}), flush=True)
 
 
+def decode_loop(torch, pp, dev, layers=32, steps=32, doc=12000, P=256, H=32, D=128, seed=1003, rope_base=1e6):
+    """The answer loop of a 12000-token document with 256 streams: 32 steps of
+    32 layers, each step appending one slot per stream (ids and plan once per
+    step, then per layer: rotary embedding at the shared positions, append,
+    attention).  Timed eagerly and as one captured HIP graph of the step
+    replayed every step (the step's start lives on the device).  The q/k/v
+    inputs of a layer are reused from step to step here (values do not change
+    the work); the parity tests use fresh ones."""
+    from workloads import decode_loop_layout
+
+    ids_full, q_lens, base0 = decode_loop_layout(doc, P, steps, seed)
+    cap = len(ids_full)
+    ids = ids_full.copy()
+    ids[base0:] = 0
+    sid = torch.from_numpy(ids).to(dev)
+    g = torch.Generator(device=dev).manual_seed(seed)
+    K = torch.randn(layers, cap, H, D, generator=g, device=dev, dtype=torch.bfloat16)
+    V = torch.randn(layers, cap, H, D, generator=g, device=dev, dtype=torch.bfloat16)
+    qkv = torch.randn(layers, 3, P, H, D, generator=g, device=dev, dtype=torch.bfloat16)
+    outs = torch.empty(layers, P, H, D, device=dev, dtype=torch.bfloat16)
+    base = torch.tensor([base0], dtype=torch.int32, device=dev)
+    plan = (torch.zeros(2, dtype=torch.int32, device=dev), torch.zeros(P, dtype=torch.int32, device=dev),
+            torch.zeros(P, 256, dtype=torch.int32, device=dev))
+    ws = torch.empty(pp.workspace_bytes(cap, P, H, D, torch.bfloat16), dtype=torch.uint8, device=dev)
+    scale = 1.0 / math.sqrt(D)
+
+    def one_step():
+        pp.pp_step_plan(sid, base, P, max_seq_len=cap, plan=plan)
+        for i in range(layers):
+            pp.pp_attn_decode_append(qkv[i, 0], qkv[i, 1], qkv[i, 2], K[i], V[i], sid, plan, scale=scale,
+                                     rope_base=rope_base, out=outs[i], workspace=ws, max_seq_len=cap)
+        base.add_(P)
+
+    def timed(fn):
+        base.fill_(base0)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        assert int(base.item()) == base0 + steps * P
+        return a.elapsed_time(b)
+
+    timed(one_step)  # warm-up pass over the whole loop
+    eager_ms = timed(one_step)
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        one_step()
+    torch.cuda.synchronize()
+    timed(graph.replay)
+    graph_ms = timed(graph.replay)
+    # KV bytes the loop reads: every layer-step reads the document and each
+    # stream's own slots (its question and the answers so far, new one included)
+    tail_slots = sum(sum(q_lens) + P * (t + 1) for t in range(steps))
+    kv_bytes = layers * (steps * doc + tail_slots) * H * D * 2 * 2
+    return {
+        "workload": f"codellama7b_doc12k_p{P}_{layers}layers_{steps}steps",
+        "layers": layers, "steps": steps, "P": P, "doc_len": doc, "rope_base": rope_base,
+        "seq_len_first_last": [base0 + P, base0 + steps * P],
+        "graph_ms_total": graph_ms, "eager_ms_total": eager_ms,
+        "graph_ms_per_step": graph_ms / steps, "eager_ms_per_step": eager_ms / steps,
+        "graph_us_per_layer_step": graph_ms / steps / layers * 1e3,
+        "answer_tok_s_graph": P * steps / (graph_ms / 1e3),
+        "effective_kv_gbs_graph": kv_bytes / (graph_ms / 1e3) / 1e9,
+        "effective_kv_hbm_frac_graph": kv_bytes / (graph_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+        "inputs": "per-layer q/k/v reused across steps; caches N(0,1) bf16 from a seeded device generator",
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -171,6 +243,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-batched", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--no-decode-loop", action="store_true",
+                    help="skip the 32-step x 32-layer appending loop (eager and graph-replayed)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -295,6 +369,12 @@ def main():
         "traffic": dom_traffic,
     }
 
+    loop = None
+    if not args.no_decode_loop:
+        log("bench: 32-step x 32-layer appending loop")
+        loop = decode_loop(torch, pp, dev)
+        torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: CPU oracle baseline")
@@ -328,6 +408,7 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
         "batched_baseline": batched,
+        "decode_loop": loop,
         "cpu_baseline": cpu,
         "kernel_source_digest": kernel_source_digest(),
     }
