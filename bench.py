@@ -229,6 +229,51 @@ def decode_loop(torch, pp, dev, layers=32, steps=32, doc=12000, P=256, H=32, D=1
     }
 
 
+def answer_sweep(torch, pp, dev, lengths=(128, 256, 512, 1024), doc=8192, P=128, H=32, D=128, seed=1005):
+    """Long answers: an 8k-token document with 128 questions (16-32 tokens)
+    and 128-1,024 answer tokens per stream already cached; one step through
+    pp_attn_decode and through the per-question baseline."""
+    import numpy as np
+
+    from workloads import canonical_layout
+
+    rows = []
+    for a in lengths:
+        rng = np.random.Generator(np.random.PCG64(seed ^ a))
+        q_lens = [int(x) for x in rng.integers(16, 33, size=P)]
+        ids, _ = canonical_layout(doc, q_lens, [a] * P)
+        T = len(ids)
+        g = torch.Generator(device=dev).manual_seed(seed + a)
+        q = torch.randn(P, H, D, generator=g, device=dev, dtype=torch.bfloat16)
+        k = torch.randn(T, H, D, generator=g, device=dev, dtype=torch.bfloat16)
+        v = torch.randn(T, H, D, generator=g, device=dev, dtype=torch.bfloat16)
+        sid = torch.from_numpy(ids).to(dev)
+        out = torch.empty_like(q)
+        ws = torch.empty(pp.workspace_bytes(T, P, H, D, torch.bfloat16), dtype=torch.uint8, device=dev)
+
+        def t(fn, n, warm):
+            for _ in range(warm):
+                fn(q, k, v, sid, seq_len=T, out=out, workspace=ws)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(n):
+                fn(q, k, v, sid, seq_len=T, out=out, workspace=ws)
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / n
+
+        dm = t(pp.pp_attn_decode, 10, 2)
+        bm = t(pp.pp_attn_decode_batched, 3, 1)
+        kv = T * H * D * 2 * 2
+        rows.append({"answer_len": a, "seq_len": T, "decode_ms": dm, "batched_ms": bm, "speedup": bm / dm,
+                     "effective_kv_gbs": kv / (dm / 1e3) / 1e9})
+        del q, k, v, sid, out, ws
+        torch.cuda.empty_cache()
+    return {"workload": f"codellama7b_doc8k_p{P}_answers{lengths[0]}-{lengths[-1]}", "P": P, "doc_len": doc,
+            "questions": "uniform 16-32", "rows": rows}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -245,6 +290,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-decode-loop", action="store_true",
                     help="skip the 32-step x 32-layer appending loop (eager and graph-replayed)")
+    ap.add_argument("--no-answer-sweep", action="store_true",
+                    help="skip the long-answer sweep (8k document, 128 streams, 128-1024 answer tokens)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -375,6 +422,11 @@ def main():
         loop = decode_loop(torch, pp, dev)
         torch.cuda.empty_cache()
 
+    sweep = None
+    if not args.no_answer_sweep:
+        log("bench: long-answer sweep")
+        sweep = answer_sweep(torch, pp, dev)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: CPU oracle baseline")
@@ -409,6 +461,7 @@ def main():
         "roofline": roofline,
         "batched_baseline": batched,
         "decode_loop": loop,
+        "answer_sweep": sweep,
         "cpu_baseline": cpu,
         "kernel_source_digest": kernel_source_digest(),
     }

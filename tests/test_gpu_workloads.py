@@ -5,6 +5,10 @@ streams {1, 7, 128, 512}, questions uniform 1-128, answers uniform 0-64,
 1% of K elements x50 (peaked softmax).  Checked on sampled streams, all
 heads.
 
+Long answers: an 8k-token document with 128 questions and 128 to 1,024
+answer tokens per stream already in the cache, sampled streams, both entry
+points.
+
 Decode loop: 32 answer steps; at each step every stream appends one K/V
 slot (its own id) and then attends, over independent layers.  A reduced copy
 (512-token document, 16 streams, 4 layers) is checked at every step; the
@@ -17,7 +21,7 @@ import torch
 import shared_prefix_stream_amd as pp
 from oracle import oracle_decode
 from tests.gpu_helpers import assert_close, reference, run, say
-from workloads import decode_loop_layout, decode_loop_step_inputs, ragged_case
+from workloads import decode_loop_layout, decode_loop_step_inputs, long_answer_case, ragged_case
 
 pytestmark = pytest.mark.gpu
 
@@ -34,6 +38,15 @@ def _sample_streams(P, rng, n=8):
 def test_ragged_sweep(doc, P):
     case = ragged_case(doc, P, seed=5000 + doc + P)
     streams = _sample_streams(P, np.random.default_rng(doc * 7 + P))
+    ref = reference(case, streams)
+    for entry in ("decode", "batched"):
+        assert_close(run(case, entry), ref, streams, what=f"{case.name} {entry}")
+
+
+@pytest.mark.parametrize("answer_len", [128, 1024])
+def test_long_answers(answer_len):
+    case = long_answer_case(answer_len, seed=6000 + answer_len)
+    streams = _sample_streams(case.P, np.random.default_rng(answer_len), n=6)
     ref = reference(case, streams)
     for entry in ("decode", "batched"):
         assert_close(run(case, entry), ref, streams, what=f"{case.name} {entry}")

@@ -207,6 +207,16 @@ def ragged_case(doc_len: int, P: int, seed: int, H: int = 32, D: int = 128) -> C
                      name=f"ragged_doc{doc_len}_p{P}")
 
 
+def long_answer_case(answer_len: int, seed: int, doc_len: int = 8192, P: int = 128, H: int = 32,
+                     D: int = 128) -> Case:
+    """Long-answer sweep member: an 8k-token document with 128 questions
+    (uniform 16-32 tokens) and `answer_len` answer tokens already decoded per
+    stream (the pages sweep answers up to 1,024 tokens at this shape)."""
+    rng = np.random.Generator(np.random.PCG64(seed ^ 0x10A6))
+    return make_case(H, D, doc_len, _uniform_ints(rng, 16, 32, P), [answer_len] * P, dtype=torch.bfloat16,
+                     seed=seed, name=f"codellama7b_doc{doc_len // 1024}k_p{P}_answers{answer_len}")
+
+
 WORKLOADS: Dict[str, object] = {
     "tiny_f32_h4_d64_doc256_p4": _tiny_f32,
     "codellama7b_doc8k_p64": _doc8k_p64,
