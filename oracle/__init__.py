@@ -13,3 +13,4 @@ from .pp_step_oracle import (  # noqa: F401
     round_bf16,
     shared_positions,
 )
+from .pp_prefill_oracle import oracle_prefill, prefill_visible  # noqa: F401
