@@ -206,6 +206,27 @@ pp_status_t pp_attn_decode_append(const void* q, const void* k_new, const void* 
                                   pp_dtype_t dtype, void* workspace, size_t workspace_bytes,
                                   void* hip_stream);
 
+/* Prefill of the whole packed request -- the document and every stream's
+ * question tokens as one sequence, attended once (Parallel Prompting project
+ * page, "How it works" and its illustration: the document and all questions
+ * go into one request, prefilled together).  Every slot i < seq_len is a
+ * query, and it attends under the same stream rule, causally:
+ *   V(i) = { j <= i : stream_id[j] == 0 || stream_id[j] == stream_id[i] }
+ *   out[i,h,:] = sum_{j in V(i)} softmax_j(scale * dot(q[i,h,:], k[j,h,:])) * v[j,h,:]
+ * A document slot sees the document up to itself; a stream's slot sees the
+ * whole document before it and its own stream's slots up to itself (never
+ * another stream's).  Layouts: q, k, v, out [seq_len, H, d] of `dtype`,
+ * stream_id [seq_len] int32, contiguous, 16-byte aligned, device memory;
+ * seq_len <= 65535 * 256.  The leading run of id-0 slots is contracted on
+ * the matrix cores in query tiles (causal inside the run); each slot's
+ * remaining visible slots past that run are compacted from stream_id and
+ * gathered.  Workspace: pp_attn_prefill_workspace_bytes(seq_len, H, d,
+ * dtype) bytes.  Contract, asynchrony and errors as pp_attn_decode. */
+size_t pp_attn_prefill_workspace_bytes(int64_t seq_len, int32_t H, int32_t d, pp_dtype_t dtype);
+pp_status_t pp_attn_prefill(const void* q, const void* k, const void* v, const int32_t* stream_id,
+                            int64_t seq_len, int32_t H, int32_t d, float scale, void* out,
+                            pp_dtype_t dtype, void* workspace, size_t workspace_bytes, void* hip_stream);
+
 /* Profiling variant of pp_attn_decode (batched == 0) or pp_attn_decode_batched
  * (batched != 0): identical arguments, contract and results, and it also
  * records caller-created hipEvent_t events on hip_stream around its kernel

@@ -34,6 +34,8 @@ __all__ = [
     "pp_attn_decode_planned",
     "pp_step_plan",
     "pp_attn_decode_append",
+    "prefill_workspace_bytes",
+    "pp_attn_prefill",
     "PP_OK",
     "PP_ERR_INVALID_ARG",
     "PP_ERR_UNSUPPORTED",
@@ -100,6 +102,10 @@ def _load():
     lib.pp_attn_decode_append.restype = ctypes.c_int
     lib.pp_attn_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, f32, ctypes.c_double, vp, vp,
                                           vp, i64, vp, ctypes.c_int, vp, sz, vp]
+    lib.pp_attn_prefill_workspace_bytes.restype = sz
+    lib.pp_attn_prefill_workspace_bytes.argtypes = [i64, i32, i32, ctypes.c_int]
+    lib.pp_attn_prefill.restype = ctypes.c_int
+    lib.pp_attn_prefill.argtypes = [vp, vp, vp, vp, i64, i32, i32, f32, vp, ctypes.c_int, vp, sz, vp]
     _lib = lib
     return lib
 
@@ -348,4 +354,47 @@ def pp_attn_decode_append(q, k_new, v_new, k_cache, v_cache, stream_id, plan, sc
         slots.data_ptr() if cap > 0 else None, cap, out.data_ptr(), code, workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _stream_handle(q.device))
     _check(st)
+    return out
+
+
+def prefill_workspace_bytes(seq_len: int, H: int, d: int, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    n = int(_load().pp_attn_prefill_workspace_bytes(int(seq_len), int(H), int(d), code))
+    if n == 0:
+        raise ValueError(f"invalid prefill shape seq_len={seq_len} H={H} d={d}")
+    return n
+
+
+def pp_attn_prefill(q, k, v, stream_id, seq_len: Optional[int] = None, scale: Optional[float] = None, out=None,
+                    workspace=None):
+    """Prefill of the packed request: every slot i < seq_len attends to the
+    slots j <= i holding the document (id 0) or its own id.  q, k, v
+    [T >= seq_len, H, d] on the GPU; returns out [T, H, d] (rows >= seq_len
+    untouched) without synchronising."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v), ("stream_id", stream_id)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if q.dim() != 3 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k and v must share one [T, H, d] shape")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k and v must share one dtype")
+    if stream_id.dtype != torch.int32 or stream_id.dim() != 1:
+        raise ValueError("stream_id must be a 1-D int32 tensor")
+    T, H, d = q.shape
+    seq_len = T if seq_len is None else int(seq_len)
+    if not (1 <= seq_len <= T) or stream_id.shape[0] < seq_len:
+        raise ValueError(f"seq_len={seq_len} must be in [1, {T}] and <= len(stream_id)")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    code = _dtype_code(q.dtype)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_cuda or not out.is_contiguous():
+        raise ValueError("out must be a contiguous GPU tensor shaped and typed like q")
+    if workspace is None:
+        workspace = torch.empty(prefill_workspace_bytes(seq_len, H, d, code), dtype=torch.uint8, device=q.device)
+    _check(_load().pp_attn_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), stream_id.data_ptr(), seq_len, H, d,
+                                   scale, out.data_ptr(), code, workspace.data_ptr(),
+                                   workspace.numel() * workspace.element_size(), _stream_handle(q.device)))
     return out

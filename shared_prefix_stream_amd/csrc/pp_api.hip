@@ -195,6 +195,38 @@ pp_status_t decode_impl(Path path, const void* q, const void* k, const void* v, 
   return ok();
 }
 
+// Prefill workspace: the one-stream plan (document length), then one
+// partial state per (slot, head) of the causal document kernel (one split).
+constexpr int64_t kPrefillMaxLen = (int64_t)65535 * 256;  // query tiles per head fit the grid
+
+size_t prefill_bytes(int64_t T, int32_t H, int32_t d) {
+  return 256 /*base alignment slack*/ + 512 /*plan, counts*/ + pp::align_up((size_t)T * H * sizeof(float2), 256) +
+         pp::align_up((size_t)T * H * d * sizeof(float), 256);
+}
+
+pp::Workspace carve_prefill(void* ws, int64_t T, int32_t H) {
+  uintptr_t at = pp::align_up((uintptr_t)ws, 256);
+  pp::Workspace w;
+  w.plan = reinterpret_cast<int32_t*>(at);
+  w.counts = reinterpret_cast<int32_t*>(at + 256);
+  w.slots = nullptr;
+  w.cap = 0;
+  at += 512;
+  w.part_ml = reinterpret_cast<float2*>(at);
+  at += pp::align_up((size_t)T * H * sizeof(float2), 256);
+  w.part_o = reinterpret_cast<float*>(at);
+  w.q_rot = nullptr;
+  return w;
+}
+
+pp_status_t check_prefill_shape(int64_t seq_len, int32_t H, int32_t d, pp_dtype_t dtype) {
+  pp_status_t st = check_shape(seq_len, 1, H, d, dtype);
+  if (st != PP_OK) return st;
+  if (seq_len > kPrefillMaxLen)
+    return fail(PP_ERR_INVALID_ARG, "prefill seq_len=%lld exceeds %lld", (long long)seq_len, (long long)kPrefillMaxLen);
+  return PP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -280,6 +312,49 @@ pp_status_t pp_attn_decode_append(const void* q, const void* k_new, const void* 
   const AppendArgs ap{k_new, v_new, rope_base};
   return decode_impl(Path::kParallel, q, k_cache, v_cache, stream_id, max_seq_len, P, H, d, scale, out, dtype,
                      workspace, workspace_bytes, hip_stream, nullptr, &xp, &ap);
+}
+
+size_t pp_attn_prefill_workspace_bytes(int64_t seq_len, int32_t H, int32_t d, pp_dtype_t dtype) {
+  if (check_prefill_shape(seq_len, H, d, dtype) != PP_OK) return 0;
+  ok();
+  return prefill_bytes(seq_len, H, d);
+}
+
+pp_status_t pp_attn_prefill(const void* q, const void* k, const void* v, const int32_t* stream_id, int64_t seq_len,
+                            int32_t H, int32_t d, float scale, void* out, pp_dtype_t dtype, void* workspace,
+                            size_t workspace_bytes, void* hip_stream) {
+  pp_status_t st = check_prefill_shape(seq_len, H, d, dtype);
+  if (st != PP_OK) return st;
+  if (!q || !k || !v || !stream_id || !out) return fail(PP_ERR_INVALID_ARG, "null q, k, v, stream_id or out");
+  if (!isfinite(scale)) return fail(PP_ERR_INVALID_ARG, "scale is not finite");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(stream_id) || !aligned16(out))
+    return fail(PP_ERR_INVALID_ARG, "q, k, v, stream_id and out must be 16-byte aligned");
+  const size_t n = (size_t)seq_len * H * d * elem_size(dtype), nid = (size_t)seq_len * 4;
+  if (overlaps(out, n, q, n) || overlaps(out, n, k, n) || overlaps(out, n, v, n) || overlaps(out, n, stream_id, nid) ||
+      overlaps(out, n, workspace, workspace_bytes))
+    return fail(PP_ERR_INVALID_ARG, "out overlaps an input or the workspace");
+  if (overlaps(workspace, workspace_bytes, q, n) || overlaps(workspace, workspace_bytes, k, n) ||
+      overlaps(workspace, workspace_bytes, v, n) || overlaps(workspace, workspace_bytes, stream_id, nid))
+    return fail(PP_ERR_INVALID_ARG, "workspace overlaps an input");
+  const size_t need = prefill_bytes(seq_len, H, d);
+  if (!workspace || workspace_bytes < need)
+    return fail(PP_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : (size_t)0, need);
+  int cus = 0;
+  if (!num_cus(&cus)) return fail(PP_ERR_HIP, "could not query the current device's compute-unit count");
+  if (cus > kSizingCus) cus = kSizingCus;
+  pp::DocPlan pl = pp::choose_doc_plan(seq_len, (int)seq_len, H, d, dtype, cus);
+  pl.n_splits = 1;  // the causal document kernel covers each query tile's prefix in one workgroup
+  const int tile = pp::doc_query_tile(pl, dtype);
+  hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  const float c = (float)((double)scale * 1.4426950408889634074);
+  const pp::Workspace ws = carve_prefill(workspace, seq_len, H);
+  // the document length (a one-stream plan with no list), the causal
+  // document part, then everything else per query slot
+  hipError_t e = pp::launch_plan(stream_id, seq_len, 1, ws.plan, ws.counts, nullptr, 0, stream);
+  if (e == hipSuccess) e = pp::launch_doc(pl, q, k, v, seq_len, (int)seq_len, H, d, dtype, c, ws, stream, true);
+  if (e == hipSuccess) e = pp::launch_prefill_rest(1, tile, q, k, v, stream_id, seq_len, H, d, dtype, c, ws, out, stream);
+  if (e != hipSuccess) return fail(PP_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
 }
 
 pp_status_t pp_attn_decode_profiled(int32_t batched, const void* q, const void* k_cache, const void* v_cache,

@@ -134,7 +134,13 @@ __device__ __forceinline__ void wait_vmcnt() {
 // workgroup's query tile (16*QB*NW queries).  With 8 waves of 32 queries
 // two waves share each SIMD, so one wave's softmax overlaps the other's
 // matrix products.
-template <int D, int QB, int NW>
+//
+// CAUSAL (prefill): query i is slot i of the sequence, and query tile pt
+// attends to the document slots j < min((pt + 1) * tile, doc_len) with
+// j <= i -- the part of every query's visible set that lies in the shared
+// document prefix up to its own tile.  One split per tile; tiles are taken
+// longest first.
+template <int D, int QB, int NW, bool CAUSAL>
 __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int P,
     int H, float c, const int32_t* __restrict__ plan, int64_t seq_len, int n_splits,
@@ -149,7 +155,8 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) unsigned char ring[NS][TL::STAGE_BYTES];
   __shared__ int redo;
 
-  const int split = blockIdx.x, h = blockIdx.y, pt = blockIdx.z;
+  const int split = blockIdx.x, h = blockIdx.y;
+  const int pt = CAUSAL ? (int)gridDim.z - 1 - (int)blockIdx.z : (int)blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int ln = lane & 15, lg = lane >> 4;
   const int q0 = pt * (16 * QB * NW) + wave * (16 * QB);
@@ -168,7 +175,8 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
       qw[qb][kc] = *reinterpret_cast<const u32x4*>(q + ((int64_t)pc * H + h) * D + kc * 32 + lg * 8);
   }
 
-  const int L = (int)min<int64_t>(load_doc_len(plan), seq_len);  // a plan never exceeds the slots given
+  int L = (int)min<int64_t>(load_doc_len(plan), seq_len);  // a plan never exceeds the slots given
+  if constexpr (CAUSAL) L = min(L, (pt + 1) * (16 * QB * NW));
   // floor(i * n_tiles / n_splits) as i * (n / k) + i * (n % k) / k: 32-bit
   // arithmetic only (i <= n_splits <= 256)
   const uint32_t n_tiles = ((uint32_t)L + NK - 1) / NK;
@@ -319,7 +327,9 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
   uint32_t pb[QB][CH][4];  // P^T as packed bf16 pairs: the P.V B operand
   auto softmax = [&](int t) __attribute__((always_inline)) {
     const int kbase = t * NK;
-    if (__builtin_expect(kbase + NK > key_end, 0)) {  // ragged last tile of the split (uniform)
+    // ragged last tile of the split, or (CAUSAL) a tile with keys past the
+    // wave's first query (uniform)
+    if (__builtin_expect(kbase + NK > key_end || (CAUSAL && kbase + NK - 1 > q0), 0)) {
       // the empty asm keeps this rare block a branch: without it the compiler
       // turns the masking into compares and selects run on every tile
       asm volatile("" ::: "memory");
@@ -330,7 +340,7 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int key = 32 * (kb >> 1) + 8 * lg + 4 * (kb & 1) + i;
-            if (kbase + key >= key_end) s[qb][kb][i] = -INFINITY;
+            if (kbase + key >= key_end || (CAUSAL && kbase + key > q0 + qb * 16 + ln)) s[qb][kb][i] = -INFINITY;
           }
     }
     // running maxima: lane (query ln, group lg) holds 4*KB keys of its query;
@@ -380,7 +390,7 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
   // fast pass: p = exp2(x) with the fixed reference 0
   auto softmax_fast = [&](int t) __attribute__((always_inline)) {
     const int kbase = t * NK;
-    if (__builtin_expect(kbase + NK > key_end, 0)) {  // ragged last tile of the split (uniform)
+    if (__builtin_expect(kbase + NK > key_end || (CAUSAL && kbase + NK - 1 > q0), 0)) {  // as in softmax
       asm volatile("" ::: "memory");  // (kept a branch, as in softmax)
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
@@ -389,7 +399,7 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int key = 32 * (kb >> 1) + 8 * lg + 4 * (kb & 1) + i;
-            if (kbase + key >= key_end) s[qb][kb][i] = -INFINITY;
+            if (kbase + key >= key_end || (CAUSAL && kbase + key > q0 + qb * 16 + ln)) s[qb][kb][i] = -INFINITY;
           }
     }
 #pragma unroll
@@ -580,7 +590,7 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
 // reads it by broadcast: the document is still read once for all streams.
 constexpr int kF32NK = 32;
 
-template <int D>
+template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kDocThreads) void doc_valu_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v, int P, int H, float c,
     const int32_t* __restrict__ plan, int64_t seq_len, int n_splits, float* __restrict__ part_o,
@@ -589,8 +599,10 @@ __global__ __launch_bounds__(kDocThreads) void doc_valu_f32_kernel(
   __shared__ __attribute__((aligned(16))) float lv[kF32NK][D];
   const int split = blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x;
-  const int p = blockIdx.z * kDocThreads + tid;
-  const int L = (int)min<int64_t>(load_doc_len(plan), seq_len);  // a plan never exceeds the slots given
+  const int pt = CAUSAL ? (int)gridDim.z - 1 - (int)blockIdx.z : (int)blockIdx.z;
+  const int p = pt * kDocThreads + tid;
+  int L = (int)min<int64_t>(load_doc_len(plan), seq_len);  // a plan never exceeds the slots given
+  if constexpr (CAUSAL) L = min(L, (pt + 1) * kDocThreads);  // see doc_mfma_bf16_kernel
   const int n_tiles = (L + kF32NK - 1) / kF32NK;
   const int t0 = (int)((int64_t)split * n_tiles / n_splits);
   const int t1 = (int)((int64_t)(split + 1) * n_tiles / n_splits);
@@ -626,7 +638,7 @@ __global__ __launch_bounds__(kDocThreads) void doc_valu_f32_kernel(
       float d = 0.f;
 #pragma unroll
       for (int e = 0; e < D; ++e) d = fmaf(qv[e], lk[j][e], d);
-      x[j] = (kbase + j < key_end) ? d * c : -INFINITY;
+      x[j] = (kbase + j < key_end && (!CAUSAL || kbase + j <= p)) ? d * c : -INFINITY;
       tmax = fmaxf(tmax, x[j]);
     }
     const float mn = fmaxf(m, tmax);
@@ -683,16 +695,22 @@ DocPlan choose_doc_plan(int64_t seq_len, int P, int H, int d, pp_dtype_t dtype, 
   return pl;
 }
 
+int doc_query_tile(const DocPlan& pl, pp_dtype_t dtype) {
+  return dtype == PP_BF16 ? 16 * pl.qb * pl.nw : kDocThreads;
+}
+
 hipError_t launch_doc(const DocPlan& pl, const void* q, const void* k, const void* v, int64_t seq_len, int P, int H,
-                      int d, pp_dtype_t dtype, float c, const Workspace& ws, hipStream_t stream) {
+                      int d, pp_dtype_t dtype, float c, const Workspace& ws, hipStream_t stream, bool causal) {
   const dim3 grid(pl.n_splits, H, pl.n_ptiles);
   if (dtype == PP_BF16) {
     auto* qq = static_cast<const uint16_t*>(q);
     auto* kk = static_cast<const uint16_t*>(k);
     auto* vv = static_cast<const uint16_t*>(v);
-#define PP_DOC_LAUNCH(DD, QQ, WW)                                                                      \
-  doc_mfma_bf16_kernel<DD, QQ, WW><<<grid, 64 * WW, 0, stream>>>(qq, kk, vv, P, H, c, ws.plan, \
-                                                                  seq_len, pl.n_splits, ws.part_o, ws.part_ml)
+#define PP_DOC_LAUNCH(DD, QQ, WW)                                                                           \
+  (causal ? doc_mfma_bf16_kernel<DD, QQ, WW, true><<<grid, 64 * WW, 0, stream>>>(                                 \
+                qq, kk, vv, P, H, c, ws.plan, seq_len, pl.n_splits, ws.part_o, ws.part_ml)                        \
+          : doc_mfma_bf16_kernel<DD, QQ, WW, false><<<grid, 64 * WW, 0, stream>>>(                                \
+                qq, kk, vv, P, H, c, ws.plan, seq_len, pl.n_splits, ws.part_o, ws.part_ml))
     // dispatch on the exact (d, 16-query blocks per wave, waves) triple
     const int cfg = d * 10000 + pl.qb * 100 + pl.nw;
     switch (cfg) {
@@ -709,10 +727,16 @@ hipError_t launch_doc(const DocPlan& pl, const void* q, const void* k, const voi
     auto* qq = static_cast<const float*>(q);
     auto* kk = static_cast<const float*>(k);
     auto* vv = static_cast<const float*>(v);
-    if (d == 128)
-      doc_valu_f32_kernel<128><<<grid, kDocThreads, 0, stream>>>(qq, kk, vv, P, H, c, ws.plan, seq_len, pl.n_splits, ws.part_o, ws.part_ml);
-    else
-      doc_valu_f32_kernel<64><<<grid, kDocThreads, 0, stream>>>(qq, kk, vv, P, H, c, ws.plan, seq_len, pl.n_splits, ws.part_o, ws.part_ml);
+#define PP_F32_LAUNCH(DD, CC) \
+  doc_valu_f32_kernel<DD, CC><<<grid, kDocThreads, 0, stream>>>(qq, kk, vv, P, H, c, ws.plan, seq_len, pl.n_splits, ws.part_o, ws.part_ml)
+    if (d == 128) {
+      if (causal) PP_F32_LAUNCH(128, true);
+      else PP_F32_LAUNCH(128, false);
+    } else {
+      if (causal) PP_F32_LAUNCH(64, true);
+      else PP_F32_LAUNCH(64, false);
+    }
+#undef PP_F32_LAUNCH
   }
   return hipGetLastError();
 }

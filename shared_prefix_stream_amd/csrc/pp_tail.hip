@@ -84,13 +84,17 @@ __device__ __forceinline__ void merge_state(float& M, float& Ls, float* A, float
   M = Mn;
 }
 
-template <typename T, int D>
+// PREFILL: blockIdx.x is a query slot i (q, out and the partials have one
+// row per slot), and its list is compacted here from stream_id: the slots
+// j in [min((i / tile + 1) * tile, doc_len), i] with id 0 or id[i] -- what
+// the causal document kernel did not cover of i's visible set.
+template <typename T, int D, bool PREFILL>
 // (at most 128 VGPRs: four workgroups per CU)
 __global__ __launch_bounds__(kTailThreads, 4) void tail_merge_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ sid,
     int64_t seq_len, int P, int H, float c, const int32_t* __restrict__ plan, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ slots, int64_t cap, int n_splits, const float* __restrict__ part_o,
-    const float2* __restrict__ part_ml, T* __restrict__ out, const int32_t* __restrict__ dyn_len) {
+    const float2* __restrict__ part_ml, T* __restrict__ out, const int32_t* __restrict__ dyn_len, int tile) {
   using S = TailShape<T, D>;
   constexpr int VEC = S::VEC, LPH = S::LPH, HPI = S::HPI, GW = S::GW;
   constexpr int RED = kTailNI * (VEC + 2);  // floats per lane in the substream merge
@@ -201,6 +205,18 @@ __global__ __launch_bounds__(kTailThreads, 4) void tail_merge_kernel(
     }
   };
   // (wave-uniform: stated so the gather loop's control stays on the scalar unit)
+  if constexpr (PREFILL) {
+    const int s1 = __builtin_amdgcn_readfirstlane(sid[s]);
+    int64_t from = min<int64_t>((int64_t)(s / tile + 1) * tile, load_doc_len(plan));
+    const int64_t len = (int64_t)s + 1;
+    while (from < len) {
+      int64_t next;
+      const int n = collect_visible<kTailThreads, kTailScanU>(sid, from, len, s1, list, kTailCap, &next, scan);
+      gather(list, n);
+      from = next;
+      __syncthreads();  // list[] is refilled by the next round
+    }
+  } else {
   const int count = __builtin_amdgcn_readfirstlane(counts[s]);
   if (count <= cap) {
     gather(slots + (int64_t)s * cap, count);  // the plan's list (global, L2-resident)
@@ -216,6 +232,7 @@ __global__ __launch_bounds__(kTailThreads, 4) void tail_merge_kernel(
       from = next;
       __syncthreads();  // list[] is refilled by the next round
     }
+  }
   }
 
   // ---- merge token substreams (fixed order 0, 1, ..., NTS-1) -----------------
@@ -255,14 +272,15 @@ __global__ __launch_bounds__(kTailThreads, 4) void tail_merge_kernel(
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, bool PREFILL = false>
 hipError_t launch_tail_t(int n_splits, const void* q, const void* k, const void* v, const int32_t* sid,
-                         int64_t seq_len, int P, int H, float c, const Workspace& ws, void* out, hipStream_t stream) {
+                         int64_t seq_len, int P, int H, float c, const Workspace& ws, void* out, hipStream_t stream,
+                         int tile = 0) {
   using S = TailShape<T, D>;
   const dim3 grid(P, (H + S::GW - 1) / S::GW);
-  tail_merge_kernel<T, D><<<grid, kTailThreads, 0, stream>>>(
+  tail_merge_kernel<T, D, PREFILL><<<grid, kTailThreads, 0, stream>>>(
       static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), sid, seq_len, P, H, c, ws.plan,
-      ws.counts, ws.slots, ws.cap, n_splits, ws.part_o, ws.part_ml, static_cast<T*>(out), ws.dyn_len);
+      ws.counts, ws.slots, ws.cap, n_splits, ws.part_o, ws.part_ml, static_cast<T*>(out), ws.dyn_len, tile);
   return hipGetLastError();
 }
 
@@ -276,6 +294,17 @@ hipError_t launch_tail_merge(int n_splits, const void* q, const void* k, const v
                     : launch_tail_t<uint16_t, 64>(n_splits, q, k, v, sid, seq_len, P, H, c, ws, out, stream);
   return d == 128 ? launch_tail_t<float, 128>(n_splits, q, k, v, sid, seq_len, P, H, c, ws, out, stream)
                   : launch_tail_t<float, 64>(n_splits, q, k, v, sid, seq_len, P, H, c, ws, out, stream);
+}
+
+hipError_t launch_prefill_rest(int n_splits, int tile, const void* q, const void* k, const void* v,
+                               const int32_t* sid, int64_t seq_len, int H, int d, pp_dtype_t dtype, float c,
+                               const Workspace& ws, void* out, hipStream_t stream) {
+  const int P = (int)seq_len;  // one query per slot
+  if (dtype == PP_BF16)
+    return d == 128 ? launch_tail_t<uint16_t, 128, true>(n_splits, q, k, v, sid, seq_len, P, H, c, ws, out, stream, tile)
+                    : launch_tail_t<uint16_t, 64, true>(n_splits, q, k, v, sid, seq_len, P, H, c, ws, out, stream, tile);
+  return d == 128 ? launch_tail_t<float, 128, true>(n_splits, q, k, v, sid, seq_len, P, H, c, ws, out, stream, tile)
+                  : launch_tail_t<float, 64, true>(n_splits, q, k, v, sid, seq_len, P, H, c, ws, out, stream, tile);
 }
 
 }  // namespace pp

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_function():
     names = _declared_functions()
     assert set(names) >= {"pp_attn_decode", "pp_attn_decode_batched", "pp_attn_workspace_bytes", "pp_attn_plan",
                           "pp_attn_decode_planned", "pp_step_plan", "pp_attn_decode_append",
-                          "pp_abi_version", "pp_status_string", "pp_last_error_message"}
+                          "pp_attn_prefill", "pp_attn_prefill_workspace_bytes", "pp_abi_version", "pp_status_string", "pp_last_error_message"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in ppattn.h but not exported"
 
@@ -192,6 +192,30 @@ def test_decode_append_validation():
     assert call(P=0) == pp.PP_ERR_INVALID_ARG
     assert call(max_len=6, wsb=1 << 30) == pp.PP_ERR_INVALID_ARG  # P > max_seq_len
     assert call(wsb=1024) == pp.PP_ERR_WORKSPACE
+    assert lib.pp_last_error_message().decode() != ""
+
+
+def test_prefill_validation():
+    lib = pp.raw()
+    assert lib.pp_attn_prefill_workspace_bytes(0, 4, 128, pp.PP_BF16) == 0
+    assert lib.pp_attn_prefill_workspace_bytes(100, 4, 96, pp.PP_BF16) == 0
+    assert lib.pp_attn_prefill_workspace_bytes(65535 * 256 + 1, 4, 128, pp.PP_BF16) == 0
+    n = lib.pp_attn_prefill_workspace_bytes(1000, 4, 128, pp.PP_BF16)
+    assert n >= 1000 * 4 * (128 + 2) * 4  # one fp32 partial state per (slot, head)
+
+    def call(q=Q, k=K, v=V, sid=SID, T=1000, out=OUT, ws=WS, wsb=n, scale=0.088, d=128):
+        return lib.pp_attn_prefill(q, k, v, sid, T, 4, d, scale, out, pp.PP_BF16, ws, wsb, None)
+
+    assert call(q=None) == pp.PP_ERR_INVALID_ARG
+    assert call(sid=None) == pp.PP_ERR_INVALID_ARG
+    assert call(T=0) == pp.PP_ERR_INVALID_ARG
+    assert call(d=96) == pp.PP_ERR_UNSUPPORTED
+    assert call(scale=float("nan")) == pp.PP_ERR_INVALID_ARG
+    assert call(k=K + 2) == pp.PP_ERR_INVALID_ARG             # misaligned
+    assert call(out=V + 1024) == pp.PP_ERR_INVALID_ARG        # out overlaps an input
+    assert call(ws=Q + 4096) == pp.PP_ERR_INVALID_ARG         # workspace overlaps q
+    assert call(wsb=n - 1) == pp.PP_ERR_WORKSPACE
+    assert call(ws=None) == pp.PP_ERR_WORKSPACE
     assert lib.pp_last_error_message().decode() != ""
 
 

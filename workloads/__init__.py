@@ -41,6 +41,10 @@ __all__ = [
     "named_workload",
     "WORKLOADS",
     "decode_loop_step_inputs",
+    "long_answer_case",
+    "PrefillCase",
+    "prefill_case",
+    "prefill_doc16k_p256",
 ]
 
 
@@ -215,6 +219,48 @@ def long_answer_case(answer_len: int, seed: int, doc_len: int = 8192, P: int = 1
     rng = np.random.Generator(np.random.PCG64(seed ^ 0x10A6))
     return make_case(H, D, doc_len, _uniform_ints(rng, 16, 32, P), [answer_len] * P, dtype=torch.bfloat16,
                      seed=seed, name=f"codellama7b_doc{doc_len // 1024}k_p{P}_answers{answer_len}")
+
+
+@dataclasses.dataclass
+class PrefillCase:
+    q: torch.Tensor          # [T, H, D]: one query per slot
+    k: torch.Tensor
+    v: torch.Tensor
+    stream_id: torch.Tensor  # [T] int32
+    seq_len: int
+    doc_len: int
+    H: int
+    D: int
+    scale: float
+    name: str
+
+
+def prefill_case(H: int, D: int, doc_len: int, q_lens: Sequence[int], dtype: torch.dtype = torch.bfloat16,
+                 seed: int = 0, a_lens: Optional[Sequence[int]] = None, shuffle_tail: bool = False,
+                 name: str = "") -> PrefillCase:
+    """The packed request before decoding: the document, then each stream's
+    question (and, if given, answer tokens), Q/K/V ~ N(0,1) for every slot.
+    shuffle_tail permutes the slots after the document (ids with them)."""
+    a = [0] * len(q_lens) if a_lens is None else a_lens
+    ids, _ = canonical_layout(doc_len, q_lens, a)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if shuffle_tail:
+        tail = ids[doc_len:].copy()
+        rng.shuffle(tail)
+        ids = np.concatenate([ids[:doc_len], tail]).astype(np.int32)
+    T = int(ids.shape[0])
+    q = rng.standard_normal((T, H, D), dtype=np.float32)
+    k = rng.standard_normal((T, H, D), dtype=np.float32)
+    v = rng.standard_normal((T, H, D), dtype=np.float32)
+    return PrefillCase(q=_round(q, dtype), k=_round(k, dtype), v=_round(v, dtype), stream_id=torch.from_numpy(ids),
+                       seq_len=T, doc_len=doc_len, H=H, D=D, scale=1.0 / math.sqrt(D), name=name)
+
+
+def prefill_doc16k_p256(seed: int = 1006) -> PrefillCase:
+    """Prefill of the 16k-token document with 256 questions of 8-48 tokens."""
+    rng = np.random.Generator(np.random.PCG64(seed ^ 0x5EED))
+    return prefill_case(32, 128, 16384, _uniform_ints(rng, 8, 48, 256), seed=seed,
+                        name="codellama7b_prefill_doc16k_p256")
 
 
 WORKLOADS: Dict[str, object] = {
