@@ -274,6 +274,42 @@ def answer_sweep(torch, pp, dev, lengths=(128, 256, 512, 1024), doc=8192, P=128,
             "questions": "uniform 16-32", "rows": rows}
 
 
+def prefill_bench(torch, pp, dev, doc=16384, P=256, H=32, D=128, seed=1006, runs=5):
+    """Prefill of the packed request (the 16k-token document and 256
+    questions of 8-48 tokens, one sequence): every slot attends causally
+    under the stream rule."""
+    import numpy as np
+
+    from workloads import _uniform_ints, canonical_layout
+
+    rng = np.random.Generator(np.random.PCG64(seed ^ 0x5EED))
+    q_lens = _uniform_ints(rng, 8, 48, P)
+    ids, _ = canonical_layout(doc, q_lens, [0] * P)
+    T = len(ids)
+    g = torch.Generator(device=dev).manual_seed(seed)
+    q, k, v = (torch.randn(T, H, D, generator=g, device=dev, dtype=torch.bfloat16) for _ in range(3))
+    sid = torch.from_numpy(ids).to(dev)
+    out = torch.empty_like(q)
+    ws = torch.empty(pp.prefill_workspace_bytes(T, H, D, torch.bfloat16), dtype=torch.uint8, device=dev)
+    pp.pp_attn_prefill(q, k, v, sid, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(runs):
+        pp.pp_attn_prefill(q, k, v, sid, out=out, workspace=ws)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / runs
+    # visible (query, key) pairs: the document causally, each question slot
+    # the whole document and its own question up to itself
+    pairs = doc * (doc + 1) // 2 + sum(n * doc + n * (n + 1) // 2 for n in q_lens)
+    flops = 4 * D * H * pairs
+    return {"workload": f"codellama7b_prefill_doc16k_p{P}", "seq_len": T, "doc_len": doc, "P": P,
+            "questions": "uniform 8-48", "ms": ms, "prefill_tok_s": T / (ms / 1e3),
+            "visible_pairs_per_head": pairs, "tflops": flops / (ms / 1e3) / 1e12,
+            "mfma_frac": flops / (ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -292,6 +328,8 @@ def main():
                     help="skip the 32-step x 32-layer appending loop (eager and graph-replayed)")
     ap.add_argument("--no-answer-sweep", action="store_true",
                     help="skip the long-answer sweep (8k document, 128 streams, 128-1024 answer tokens)")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the prefill of the 16k-token document with 256 questions")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -427,6 +465,12 @@ def main():
         log("bench: long-answer sweep")
         sweep = answer_sweep(torch, pp, dev)
 
+    prefill = None
+    if not args.no_prefill:
+        log("bench: prefill")
+        prefill = prefill_bench(torch, pp, dev)
+        torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: CPU oracle baseline")
@@ -462,6 +506,7 @@ def main():
         "batched_baseline": batched,
         "decode_loop": loop,
         "answer_sweep": sweep,
+        "prefill": prefill,
         "cpu_baseline": cpu,
         "kernel_source_digest": kernel_source_digest(),
     }
