@@ -30,6 +30,11 @@ Each stream is computed independently over only its visible slots; the
 shared document is never contracted once for all streams (that reuse is the
 method under test, not part of its definition).  Inputs are cast exactly to
 float64 before any arithmetic.
+
+Grouped key/value heads (the pages' real-benchmark model shares each
+key/value head among several query heads; the pages give no head counts):
+with Hq query heads and Hkv key/value heads, query head h reads key/value
+head h // (Hq / Hkv).  Hkv = Hq is the one-head-per-key case.
 """
 from __future__ import annotations
 
@@ -118,8 +123,9 @@ def oracle_decode(q, k, v, stream_id, seq_len: int, scale: float,
                   return_weights: bool = False):
     """Reference output of one decode step.
 
-    q: [P, H, d]; k, v: [T >= seq_len, H, d] (torch tensors or arrays of any
-    float dtype, cast exactly to float64); stream_id: [T] integers.
+    q: [P, H, d]; k, v: [T >= seq_len, Hkv, d] with H a multiple of Hkv
+    (torch tensors or arrays of any float dtype, cast exactly to float64);
+    stream_id: [T] integers.
     Returns out [P, H, d] float64 (rows of streams not in `streams` are NaN),
     and with `return_weights` also a dict {(s, h): (idx, w)}.
     """
@@ -130,6 +136,9 @@ def oracle_decode(q, k, v, stream_id, seq_len: int, scale: float,
     # per-head contiguous float64 copies [H, T, d] of the first seq_len slots
     kf = np.ascontiguousarray(to_f64(k[:seq_len]).transpose(1, 0, 2))
     vf = np.ascontiguousarray(to_f64(v[:seq_len]).transpose(1, 0, 2))
+    if H % kf.shape[0] != 0:
+        raise ValueError(f"{H} query heads cannot share {kf.shape[0]} key/value heads evenly")
+    G = H // kf.shape[0]  # query heads per key/value head
     streams = range(P) if streams is None else list(streams)
     heads = range(H) if heads is None else list(heads)
     out = np.full((P, H, d), np.nan)
@@ -138,9 +147,9 @@ def oracle_decode(q, k, v, stream_id, seq_len: int, scale: float,
         idx = visible_slots(ids, seq_len, s)
         for h in heads:
             if return_weights:
-                o, w = attend(qf[s, h], kf[h], vf[h], idx, scale, return_weights=True)
+                o, w = attend(qf[s, h], kf[h // G], vf[h // G], idx, scale, return_weights=True)
                 weights[(s, h)] = (idx, w)
             else:
-                o = attend(qf[s, h], kf[h], vf[h], idx, scale)
+                o = attend(qf[s, h], kf[h // G], vf[h // G], idx, scale)
             out[s, h] = o
     return (out, weights) if return_weights else out

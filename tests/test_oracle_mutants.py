@@ -24,6 +24,8 @@ MUTANTS = {
     "prefix run too long": ("r = int(np.searchsorted(idx - np.arange(idx.size), 1))",
                             "r = int(np.searchsorted(idx - np.arange(idx.size), 2))"),
     "head transposed": ("out[s, h] = o", "out[s, (h + 1) % H] = o"),
+    "grouped heads read the wrong key head": ("attend(qf[s, h], kf[h // G], vf[h // G], idx, scale)\n",
+                                              "attend(qf[s, h], kf[h % kf.shape[0]], vf[h % kf.shape[0]], idx, scale)\n"),
     "doc prefix stops late": ("return int(nz[0]) if nz.size else int(seq_len)",
                               "return int(nz[0]) + 1 if nz.size else int(seq_len)"),
 }
@@ -70,6 +72,17 @@ def _pins_pass(mod) -> bool:
     with np.errstate(all="ignore"):
         sh = mod.oracle_decode(q, kk + u[None], v, sid, c.seq_len, c.scale)
     checks.append(bool(np.all(np.isfinite(sh))) and np.allclose(sh, base, rtol=1e-9, atol=1e-9))
+    # grouped key/value heads against torch's grouped-query SDPA
+    rng = np.random.default_rng(12)
+    ids = np.array([0, 0, 0, 1, 1, 2], dtype=np.int32)
+    q, kk, v = rng.standard_normal((2, 6, 8)), rng.standard_normal((6, 2, 8)), rng.standard_normal((6, 2, 8))
+    o = mod.oracle_decode(q, kk, v, ids, 6, 0.5)
+    for s in range(2):
+        idx = np.flatnonzero((ids == 0) | (ids == s + 1))
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[s][None, :, None, :]), torch.from_numpy(kk[idx].transpose(1, 0, 2).copy())[None],
+            torch.from_numpy(v[idx].transpose(1, 0, 2).copy())[None], scale=0.5, enable_gqa=True)
+        checks.append(np.allclose(o[s], ref[0, :, 0, :].numpy(), rtol=1e-12, atol=1e-12))
     return all(bool(x) for x in checks)
 
 

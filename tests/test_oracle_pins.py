@@ -284,3 +284,42 @@ def test_only_first_seq_len_slots_are_read():
     c = make_case(2, 8, 5, [2, 3], [1, 2], dtype=torch.float32, seed=13, extra_capacity=7)
     out = oracle_decode(c.q, c.k, c.v, c.stream_id.numpy(), c.seq_len, c.scale)
     assert np.all(np.isfinite(out))
+
+
+# ---------------------------------------------- grouped key/value heads ---
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (28, 4), (6, 6)])
+def test_grouped_heads_match_sdpa(Hq, Hkv):
+    # each stream against torch's grouped-query SDPA over its own visible
+    # slots (fp64, CPU): an independent implementation of the head sharing
+    rng = np.random.default_rng(Hq * 10 + Hkv)
+    P, d = 4, 16
+    ids, own = canonical_layout(9, [2, 3, 1, 4], [1, 2, 0, 1])
+    T = len(ids)
+    q = rng.standard_normal((P, Hq, d))
+    k = rng.standard_normal((T, Hkv, d))
+    v = rng.standard_normal((T, Hkv, d))
+    got = oracle_decode(q, k, v, ids, T, 0.3)
+    for s in range(P):
+        idx = visible_slots(ids, T, s)
+        qt = torch.from_numpy(q[s][:, None, :]).unsqueeze(0)              # [1, Hq, 1, d]
+        kt = torch.from_numpy(k[idx].transpose(1, 0, 2).copy()).unsqueeze(0)  # [1, Hkv, n, d]
+        vt = torch.from_numpy(v[idx].transpose(1, 0, 2).copy()).unsqueeze(0)
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=0.3, enable_gqa=True)
+        np.testing.assert_allclose(got[s], ref[0, :, 0, :].numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_grouped_heads_equal_repeated_heads():
+    # sharing a key/value head among G query heads = giving each query head
+    # its own copy of it
+    rng = np.random.default_rng(77)
+    ids, _ = canonical_layout(5, [2, 2], [1, 1])
+    T = len(ids)
+    q = rng.standard_normal((2, 6, 8))
+    k = rng.standard_normal((T, 2, 8))
+    v = rng.standard_normal((T, 2, 8))
+    a = oracle_decode(q, k, v, ids, T, 0.5)
+    b = oracle_decode(q, np.repeat(k, 3, axis=1), np.repeat(v, 3, axis=1), ids, T, 0.5)
+    np.testing.assert_array_equal(a, b)
+    with pytest.raises(ValueError):
+        oracle_decode(q, k[:, :1].repeat(4, axis=1), v[:, :1].repeat(4, axis=1), ids, T, 0.5)
