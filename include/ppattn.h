@@ -83,6 +83,7 @@ typedef enum { PP_BF16 = 0, PP_F32 = 1 } pp_dtype_t;
 #define PP_MAX_SEQ_LEN ((int64_t)1 << 30)
 #define PP_MAX_STREAMS 65535
 #define PP_MAX_HEADS 65535
+#define PP_MAX_REQUESTS 65535
 
 /* ABI version of the loaded library (PP_ABI_VERSION at build time). */
 int pp_abi_version(void);
@@ -145,6 +146,40 @@ pp_status_t pp_attn_decode_planned(const void* q, const void* k_cache, const voi
                                    const int32_t* plan_doc_len, const int32_t* plan_counts,
                                    const int32_t* plan_slots, int64_t plan_capacity,
                                    void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Several Parallel Prompting requests in one launch, with grouped key/value
+ * heads (Parallel Prompting project page: the best number of streams per
+ * request is 16-64, so a server batches requests; its real-benchmark model
+ * shares each key/value head between several query heads).  Request b has
+ * its own document, P streams, stream ids and caches; within a request the
+ * definition of pp_attn_decode holds, with query head hq of a stream reading
+ * key/value head hq / (Hq / Hkv):
+ *   q          [B, P, Hq, d]               out [B, P, Hq, d]
+ *   k_cache,   [B, max_seq_len, Hkv, d]    (request b's slot j at row
+ *   v_cache                                 b * max_seq_len + j)
+ *   stream_id  [B, max_seq_len] int32      (per request: 0 = its document,
+ *                                           s + 1 = its stream s)
+ *   seq_lens   device int32[B]: request b's seq_len, clamped on the device to
+ *              [0, max_seq_len] (0: its streams see nothing, out is zero)
+ * Hq must be a multiple of Hkv.  The document kernel contracts each K/V tile
+ * of a request against all P * Hq / Hkv queries of its key/value head.
+ * Workspace: pp_attn_multi_workspace_bytes(max_seq_len, B, P, Hq, Hkv, d,
+ * dtype).  Other contract and errors as pp_attn_decode (PP_ERR_INVALID_ARG
+ * also for B out of [1, PP_MAX_REQUESTS], Hq % Hkv != 0, a null seq_lens, or
+ * too many query tiles for the grid).  pp_attn_decode_multi_batched is the
+ * per-question baseline of the same launch. */
+size_t pp_attn_multi_workspace_bytes(int64_t max_seq_len, int32_t B, int32_t P, int32_t Hq, int32_t Hkv,
+                                     int32_t d, pp_dtype_t dtype);
+pp_status_t pp_attn_decode_multi(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* stream_id, const int32_t* seq_lens, int64_t max_seq_len,
+                                 int32_t B, int32_t P, int32_t Hq, int32_t Hkv, int32_t d, float scale,
+                                 void* out, pp_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                 void* hip_stream);
+pp_status_t pp_attn_decode_multi_batched(const void* q, const void* k_cache, const void* v_cache,
+                                         const int32_t* stream_id, const int32_t* seq_lens,
+                                         int64_t max_seq_len, int32_t B, int32_t P, int32_t Hq, int32_t Hkv,
+                                         int32_t d, float scale, void* out, pp_dtype_t dtype,
+                                         void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* Starts a decode step in which every stream appends one slot (Parallel
  * Prompting project page, "How it works": each decode step appends one token

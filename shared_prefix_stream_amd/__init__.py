@@ -36,6 +36,8 @@ __all__ = [
     "pp_attn_decode_append",
     "prefill_workspace_bytes",
     "pp_attn_prefill",
+    "multi_workspace_bytes",
+    "pp_attn_decode_multi",
     "PP_OK",
     "PP_ERR_INVALID_ARG",
     "PP_ERR_UNSUPPORTED",
@@ -106,6 +108,12 @@ def _load():
     lib.pp_attn_prefill_workspace_bytes.argtypes = [i64, i32, i32, ctypes.c_int]
     lib.pp_attn_prefill.restype = ctypes.c_int
     lib.pp_attn_prefill.argtypes = [vp, vp, vp, vp, i64, i32, i32, f32, vp, ctypes.c_int, vp, sz, vp]
+    lib.pp_attn_multi_workspace_bytes.restype = sz
+    lib.pp_attn_multi_workspace_bytes.argtypes = [i64, i32, i32, i32, i32, i32, ctypes.c_int]
+    for name in ("pp_attn_decode_multi", "pp_attn_decode_multi_batched"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, f32, vp, ctypes.c_int, vp, sz, vp]
     _lib = lib
     return lib
 
@@ -397,4 +405,51 @@ def pp_attn_prefill(q, k, v, stream_id, seq_len: Optional[int] = None, scale: Op
     _check(_load().pp_attn_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), stream_id.data_ptr(), seq_len, H, d,
                                    scale, out.data_ptr(), code, workspace.data_ptr(),
                                    workspace.numel() * workspace.element_size(), _stream_handle(q.device)))
+    return out
+
+
+def multi_workspace_bytes(max_seq_len: int, B: int, P: int, Hq: int, Hkv: int, d: int, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    n = int(_load().pp_attn_multi_workspace_bytes(int(max_seq_len), int(B), int(P), int(Hq), int(Hkv), int(d), code))
+    if n == 0:
+        raise ValueError(f"invalid shape max_seq_len={max_seq_len} B={B} P={P} Hq={Hq} Hkv={Hkv} d={d}")
+    return n
+
+
+def pp_attn_decode_multi(q, k_cache, v_cache, stream_id, seq_lens, scale: Optional[float] = None, out=None,
+                         workspace=None, batched: bool = False):
+    """B requests in one launch, grouped key/value heads: q [B, P, Hq, d],
+    k_cache/v_cache [B, T, Hkv, d], stream_id [B, T] int32, seq_lens [B]
+    int32 (all on the GPU).  batched=True runs the per-question baseline.
+    Returns out [B, P, Hq, d] without synchronising."""
+    import torch
+
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("stream_id", stream_id),
+                    ("seq_lens", seq_lens)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if q.dim() != 4 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("q must be [B, P, Hq, d] and k_cache, v_cache [B, T, Hkv, d]")
+    B, P, Hq, d = q.shape
+    _, T, Hkv, dk = k_cache.shape
+    if k_cache.shape[0] != B or dk != d:
+        raise ValueError(f"k_cache {tuple(k_cache.shape)} does not match q {tuple(q.shape)}")
+    if not (q.dtype == k_cache.dtype == v_cache.dtype):
+        raise ValueError("q, k_cache and v_cache must share one dtype")
+    if stream_id.dtype != torch.int32 or tuple(stream_id.shape) != (B, T):
+        raise ValueError("stream_id must be an int32 [B, T] tensor")
+    if seq_lens.dtype != torch.int32 or tuple(seq_lens.shape) != (B,):
+        raise ValueError("seq_lens must be an int32 [B] tensor")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    code = _dtype_code(q.dtype)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_cuda or not out.is_contiguous():
+        raise ValueError("out must be a contiguous GPU tensor shaped and typed like q")
+    if workspace is None:
+        workspace = torch.empty(multi_workspace_bytes(T, B, P, Hq, Hkv, d, code), dtype=torch.uint8, device=q.device)
+    fn = _load().pp_attn_decode_multi_batched if batched else _load().pp_attn_decode_multi
+    _check(fn(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), stream_id.data_ptr(), seq_lens.data_ptr(), T, B, P,
+              Hq, Hkv, d, scale, out.data_ptr(), code, workspace.data_ptr(),
+              workspace.numel() * workspace.element_size(), _stream_handle(q.device)))
     return out

@@ -72,18 +72,23 @@ struct Plan {
   int batched_splits;
 };
 
-Plan plan_for(int64_t seq_len, int32_t P, int32_t H, int32_t d, pp_dtype_t dtype, int cus) {
+// B requests of P streams, H query heads in groups of G per key/value head:
+// the document kernel sees P * G queries per key/value head and B * H / G
+// (key/value head, request) pairs; the baseline B * P streams of H heads.
+Plan plan_for(int64_t seq_len, int32_t P, int32_t H, int32_t d, pp_dtype_t dtype, int cus, int32_t B = 1,
+              int32_t G = 1) {
   if (cus > kSizingCus) cus = kSizingCus;
   Plan pl;
-  pl.doc = pp::choose_doc_plan(seq_len, P, H, d, dtype, cus);
-  pl.batched_splits = pp::choose_batched_splits(seq_len, P, H, cus);
+  pl.doc = pp::choose_doc_plan(seq_len, P * G, B * (H / G), d, dtype, cus);
+  pl.batched_splits = pp::choose_batched_splits(seq_len, B * P, H, cus);
   return pl;
 }
 
-size_t required_bytes(int64_t seq_len, int32_t P, int32_t H, int32_t d, pp_dtype_t dtype) {
-  const Plan pl = plan_for(seq_len, P, H, d, dtype, kSizingCus);
+size_t required_bytes(int64_t seq_len, int32_t P, int32_t H, int32_t d, pp_dtype_t dtype, int32_t B = 1,
+                      int32_t G = 1) {
+  const Plan pl = plan_for(seq_len, P, H, d, dtype, kSizingCus, B, G);
   const int n = pl.doc.n_splits > pl.batched_splits ? pl.doc.n_splits : pl.batched_splits;
-  return pp::workspace_bytes_for(n, P, H, d, seq_len);
+  return pp::workspace_bytes_for(n, (int64_t)B * P, H, d, seq_len, B);
 }
 
 enum class Path { kParallel, kBatched };
@@ -104,10 +109,14 @@ struct AppendArgs {
   double rope_base;
 };
 
+// bt (several requests, grouped key/value heads) comes with the multi entry
+// points only, which have checked B, G and seq_lens; H is the number of
+// query heads.
 pp_status_t decode_impl(Path path, const void* q, const void* k, const void* v, const int32_t* sid, int64_t seq_len,
                         int32_t P, int32_t H, int32_t d, float scale, void* out, pp_dtype_t dtype, void* workspace,
                         size_t workspace_bytes, void* hip_stream, void* const* events = nullptr,
-                        const ExternalPlan* xp = nullptr, const AppendArgs* ap = nullptr) {
+                        const ExternalPlan* xp = nullptr, const AppendArgs* ap = nullptr,
+                        pp::Batch bt = pp::Batch()) {
   pp_status_t st = check_shape(seq_len, P, H, d, dtype);
   if (st != PP_OK) return st;
   if (!q || !k || !v || !sid || !out) return fail(PP_ERR_INVALID_ARG, "null q, k_cache, v_cache, stream_id or out");
@@ -115,7 +124,11 @@ pp_status_t decode_impl(Path path, const void* q, const void* k, const void* v, 
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(sid) || !aligned16(out))
     return fail(PP_ERR_INVALID_ARG, "q, k_cache, v_cache, stream_id and out must be 16-byte aligned");
   const size_t es = elem_size(dtype);
-  const size_t nq = (size_t)P * H * d * es, nkv = (size_t)seq_len * H * d * es, nid = (size_t)seq_len * 4;
+  const int32_t B = bt.B, G = bt.G, Hkv = H / G;
+  bt.kv_stride = seq_len * Hkv * d;
+  bt.id_stride = seq_len;
+  const size_t nq = (size_t)B * P * H * d * es, nkv = (size_t)B * seq_len * Hkv * d * es,
+               nid = (size_t)B * seq_len * 4;
   if (overlaps(out, nq, q, nq) || overlaps(out, nq, k, nkv) || overlaps(out, nq, v, nkv) ||
       overlaps(out, nq, sid, nid) || overlaps(out, nq, workspace, workspace_bytes))
     return fail(PP_ERR_INVALID_ARG, "out overlaps an input or the workspace");
@@ -153,17 +166,19 @@ pp_status_t decode_impl(Path path, const void* q, const void* k, const void* v, 
         overlaps(workspace, workspace_bytes, ap->k_new, nq) || overlaps(workspace, workspace_bytes, ap->v_new, nq))
       return fail(PP_ERR_INVALID_ARG, "k_new or v_new overlaps out or the workspace");
   }
-  const size_t need = required_bytes(seq_len, P, H, d, dtype);
+  const size_t need = required_bytes(seq_len, P, H, d, dtype, B, G);
   if (!workspace || workspace_bytes < need)
     return fail(PP_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : (size_t)0, need);
   int cus = 0;
   if (!num_cus(&cus)) return fail(PP_ERR_HIP, "could not query the current device's compute-unit count");
-  const Plan pl = plan_for(seq_len, P, H, d, dtype, cus);
+  const Plan pl = plan_for(seq_len, P, H, d, dtype, cus, B, G);
+  if ((int64_t)pl.doc.n_ptiles * B > 65535)
+    return fail(PP_ERR_INVALID_ARG, "B * query tiles = %lld exceeds the grid", (long long)pl.doc.n_ptiles * B);
 
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   const float c = (float)((double)scale * 1.4426950408889634074);  // log2(e): softmax in base 2
   const int n_splits = path == Path::kParallel ? pl.doc.n_splits : pl.batched_splits;
-  pp::Workspace ws = pp::carve_workspace(workspace, n_splits, P, H, d, seq_len);
+  pp::Workspace ws = pp::carve_workspace(workspace, n_splits, (int64_t)B * P, H, d, seq_len, B);
   if (xp) {  // the caller's plan (read only) in place of the plan kernel's
     ws.plan = const_cast<int32_t*>(xp->doc_len);
     ws.counts = const_cast<int32_t*>(xp->counts);
@@ -177,7 +192,7 @@ pp_status_t decode_impl(Path path, const void* q, const void* k, const void* v, 
     return events ? hipEventRecord(static_cast<hipEvent_t>(events[i]), stream) : hipSuccess;
   };
   hipError_t e = mark(0);
-  if (e == hipSuccess && !xp) e = pp::launch_plan(sid, seq_len, P, ws.plan, ws.counts, ws.slots, ws.cap, stream);
+  if (e == hipSuccess && !xp) e = pp::launch_plan(sid, seq_len, P, ws.plan, ws.counts, ws.slots, ws.cap, stream, bt);
   if (e == hipSuccess && ap) {  // new keys and values into the caches, rotated queries into the workspace
     e = pp::launch_append_rope(q, ap->k_new, ap->v_new, const_cast<void*>(k), const_cast<void*>(v), P, H, d, dtype,
                                ap->rope_base, ws.plan, ws.counts, seq_len, ws.q_rot, stream);
@@ -185,11 +200,13 @@ pp_status_t decode_impl(Path path, const void* q, const void* k, const void* v, 
   }
   if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess) {
-    e = path == Path::kParallel ? pp::launch_doc(pl.doc, q, k, v, seq_len, P, H, d, dtype, c, ws, stream)
-                                : pp::launch_batched_doc(n_splits, q, k, v, seq_len, P, H, d, dtype, c, ws, stream);
+    e = path == Path::kParallel
+            ? pp::launch_doc(pl.doc, q, k, v, seq_len, P, Hkv, d, dtype, c, ws, stream, false, bt)
+            : pp::launch_batched_doc(n_splits, q, k, v, seq_len, P, H, d, dtype, c, ws, stream, bt);
   }
   if (e == hipSuccess) e = mark(2);
-  if (e == hipSuccess) e = pp::launch_tail_merge(n_splits, q, k, v, sid, seq_len, P, H, d, dtype, c, ws, out, stream);
+  if (e == hipSuccess)
+    e = pp::launch_tail_merge(n_splits, q, k, v, sid, seq_len, P, H, d, dtype, c, ws, out, stream, bt);
   if (e == hipSuccess) e = mark(3);
   if (e != hipSuccess) return fail(PP_ERR_HIP, "kernel launch or event record failed: %s", hipGetErrorString(e));
   return ok();
@@ -312,6 +329,52 @@ pp_status_t pp_attn_decode_append(const void* q, const void* k_new, const void* 
   const AppendArgs ap{k_new, v_new, rope_base};
   return decode_impl(Path::kParallel, q, k_cache, v_cache, stream_id, max_seq_len, P, H, d, scale, out, dtype,
                      workspace, workspace_bytes, hip_stream, nullptr, &xp, &ap);
+}
+
+size_t pp_attn_multi_workspace_bytes(int64_t max_seq_len, int32_t B, int32_t P, int32_t Hq, int32_t Hkv, int32_t d,
+                                     pp_dtype_t dtype) {
+  if (check_shape(max_seq_len, P, Hq, d, dtype) != PP_OK) return 0;
+  if (B < 1 || B > PP_MAX_REQUESTS || Hkv < 1 || Hq % Hkv != 0) return 0;
+  ok();
+  return required_bytes(max_seq_len, P, Hq, d, dtype, B, Hq / Hkv);
+}
+
+static pp_status_t multi_impl(Path path, const void* q, const void* k, const void* v, const int32_t* sid,
+                              const int32_t* seq_lens, int64_t max_seq_len, int32_t B, int32_t P, int32_t Hq,
+                              int32_t Hkv, int32_t d, float scale, void* out, pp_dtype_t dtype, void* workspace,
+                              size_t workspace_bytes, void* hip_stream) {
+  if (B < 1 || B > PP_MAX_REQUESTS) return fail(PP_ERR_INVALID_ARG, "B=%d out of range [1, %d]", B, PP_MAX_REQUESTS);
+  if (Hkv < 1 || Hq < 1 || Hq % Hkv != 0)
+    return fail(PP_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if ((int64_t)B * P > PP_MAX_STREAMS * (int64_t)PP_MAX_REQUESTS)
+    return fail(PP_ERR_INVALID_ARG, "B * P too large");
+  if (!seq_lens) return fail(PP_ERR_INVALID_ARG, "null seq_lens");
+  pp::Batch bt;
+  bt.B = B;
+  bt.G = Hq / Hkv;
+  bt.seq_lens = seq_lens;
+  const size_t nq = (size_t)B * P * Hq * d * elem_size(dtype);
+  if (overlaps(out, nq, seq_lens, (size_t)B * 4) || overlaps(workspace, workspace_bytes, seq_lens, (size_t)B * 4))
+    return fail(PP_ERR_INVALID_ARG, "seq_lens overlaps out or the workspace");
+  return decode_impl(path, q, k, v, sid, max_seq_len, P, Hq, d, scale, out, dtype, workspace, workspace_bytes,
+                     hip_stream, nullptr, nullptr, nullptr, bt);
+}
+
+pp_status_t pp_attn_decode_multi(const void* q, const void* k_cache, const void* v_cache, const int32_t* stream_id,
+                                 const int32_t* seq_lens, int64_t max_seq_len, int32_t B, int32_t P, int32_t Hq,
+                                 int32_t Hkv, int32_t d, float scale, void* out, pp_dtype_t dtype, void* workspace,
+                                 size_t workspace_bytes, void* hip_stream) {
+  return multi_impl(Path::kParallel, q, k_cache, v_cache, stream_id, seq_lens, max_seq_len, B, P, Hq, Hkv, d, scale,
+                    out, dtype, workspace, workspace_bytes, hip_stream);
+}
+
+pp_status_t pp_attn_decode_multi_batched(const void* q, const void* k_cache, const void* v_cache,
+                                         const int32_t* stream_id, const int32_t* seq_lens, int64_t max_seq_len,
+                                         int32_t B, int32_t P, int32_t Hq, int32_t Hkv, int32_t d, float scale,
+                                         void* out, pp_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                         void* hip_stream) {
+  return multi_impl(Path::kBatched, q, k_cache, v_cache, stream_id, seq_lens, max_seq_len, B, P, Hq, Hkv, d, scale,
+                    out, dtype, workspace, workspace_bytes, hip_stream);
 }
 
 size_t pp_attn_prefill_workspace_bytes(int64_t seq_len, int32_t H, int32_t d, pp_dtype_t dtype) {

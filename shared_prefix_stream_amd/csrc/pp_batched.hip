@@ -15,7 +15,10 @@
 // stream's own slots and merges, exactly as for pp_attn_decode.  Workgroups
 // are dispatched request-major (head fastest, stream outermost), as a
 // per-request decode launch orders them; nothing co-schedules different
-// requests onto the same document tiles on purpose.
+// requests onto the same document tiles on purpose.  With grouped key/value
+// heads each query head reads its group's key/value head; with several
+// Parallel Prompting requests (grid.z = B * P) each stream reads its own
+// request's document.
 #include <math.h>
 
 #include "pp_internal.h"
@@ -57,20 +60,24 @@ template <typename T, int D>
 __global__ __launch_bounds__(kBThreads) void batched_doc_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, int P, int H, float c,
     const int32_t* __restrict__ plan, int64_t seq_len, int n_splits, float* __restrict__ part_o,
-    float2* __restrict__ part_ml) {
+    float2* __restrict__ part_ml, Batch bt) {
   constexpr int VEC = 16 / (int)sizeof(T);
   constexpr int LPK = D / VEC;   // lanes per slot
   constexpr int KPI = 64 / LPK;  // slots per wave-wide load
   constexpr int NW = kBThreads / 64;
   __shared__ float red[NW][VEC + 2][LPK];
 
-  const int h = blockIdx.x, split = blockIdx.y, s = blockIdx.z;
+  const int h = blockIdx.x, split = blockIdx.y, s = blockIdx.z;  // s: stream of the launch
+  const int b = s / P;                                             // its request
   // (the wave index is wave-uniform; readfirstlane lets the compiler know)
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int kg = lane / LPK, dl = lane % LPK;
-  const int64_t L = load_doc_len(plan);
+  const int64_t L = min<int64_t>(load_doc_len(plan + b), seq_len);
   const int64_t j_begin = split * L / n_splits, j_end = (split + 1) * L / n_splits;
-  const int64_t row = (int64_t)H * D;
+  const int64_t row = (int64_t)(H / bt.G) * D;  // key/value heads
+  const int hk = h / bt.G;
+  k += b * bt.kv_stride;
+  v += b * bt.kv_stride;
 
   float qv[VEC];
   to_f32b<T>(*reinterpret_cast<const u32x4*>(q + ((int64_t)s * H + h) * D + dl * VEC), qv);
@@ -85,7 +92,7 @@ __global__ __launch_bounds__(kBThreads) void batched_doc_kernel(
       // unconditional load (slots past the split's end re-read its last slot
       // and are skipped below), so all of them are in flight together
       const int64_t j = min(blk + (int64_t)(wave * kBU + u) * KPI + kg, j_end - 1);
-      const int64_t off = j * row + (int64_t)h * D + dl * VEC;
+      const int64_t off = j * row + (int64_t)hk * D + dl * VEC;
       kr[u] = *reinterpret_cast<const u32x4*>(k + off);
       vr[u] = *reinterpret_cast<const u32x4*>(v + off);
     }
@@ -147,7 +154,7 @@ __global__ __launch_bounds__(kBThreads) void batched_doc_kernel(
     for (int e = 0; e < VEC; ++e) a2[e] = red[w][2 + e][dl];
     merge_b<VEC>(m, l, acc, red[w][0][dl], red[w][1][dl], a2);
   }
-  const int64_t sh = ((int64_t)split * P + s) * H + h;
+  const int64_t sh = ((int64_t)split * bt.B * P + s) * H + h;
   if (dl == 0) part_ml[sh] = make_float2(m, l);
 #pragma unroll
   for (int e = 0; e < VEC; e += 4)
@@ -167,12 +174,13 @@ int choose_batched_splits(int64_t seq_len, int P, int H, int num_cus) {
 }
 
 hipError_t launch_batched_doc(int n_splits, const void* q, const void* k, const void* v, int64_t seq_len, int P,
-                              int H, int d, pp_dtype_t dtype, float c, const Workspace& ws, hipStream_t stream) {
-  const dim3 grid(H, n_splits, P);  // dispatch order: heads, then splits, stream outermost
+                              int H, int d, pp_dtype_t dtype, float c, const Workspace& ws, hipStream_t stream,
+                              const Batch& bt) {
+  const dim3 grid(H, n_splits, P * bt.B);  // dispatch order: heads, then splits, stream outermost
 #define PP_B_LAUNCH(TT, DD)                                                                                   \
   batched_doc_kernel<TT, DD><<<grid, kBThreads, 0, stream>>>(static_cast<const TT*>(q), static_cast<const TT*>(k), \
                                                              static_cast<const TT*>(v), P, H, c, ws.plan,    \
-                                                             seq_len, n_splits, ws.part_o, ws.part_ml)
+                                                             seq_len, n_splits, ws.part_o, ws.part_ml, bt)
   if (dtype == PP_BF16) {
     if (d == 128) PP_B_LAUNCH(uint16_t, 128);
     else PP_B_LAUNCH(uint16_t, 64);

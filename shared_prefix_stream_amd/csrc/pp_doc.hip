@@ -135,6 +135,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 // two waves share each SIMD, so one wave's softmax overlaps the other's
 // matrix products.
 //
+// Queries of a workgroup: the P streams' queries of the G query heads that
+// read key/value head h, query p = s * G + g for stream s and group member g
+// (grouped key/value heads: one K/V tile serves G * P queries).  Several
+// requests: grid.z = B * (query tiles per request), request-major; each
+// request has its own document length (plan[b]), caches and queries.
+//
 // CAUSAL (prefill): query i is slot i of the sequence, and query tile pt
 // attends to the document slots j < min((pt + 1) * tile, doc_len) with
 // j <= i -- the part of every query's visible set that lies in the shared
@@ -144,7 +150,7 @@ template <int D, int QB, int NW, bool CAUSAL>
 __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int P,
     int H, float c, const int32_t* __restrict__ plan, int64_t seq_len, int n_splits,
-    float* __restrict__ part_o, float2* __restrict__ part_ml) {
+    float* __restrict__ part_o, float2* __restrict__ part_ml, Batch bt) {
   using TL = DocTile<D, QB, NW>;
   constexpr int NK = TL::NK, NS = TL::NS, NLD = TL::NLD, ROWB = TL::ROWB, CPR = TL::CPR;
   constexpr int KC = D / 32;   // QK contraction steps (32 dims each)
@@ -156,11 +162,16 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
   __shared__ int redo;
 
   const int split = blockIdx.x, h = blockIdx.y;
-  const int pt = CAUSAL ? (int)gridDim.z - 1 - (int)blockIdx.z : (int)blockIdx.z;
+  const int nz = (int)gridDim.z / bt.B;  // query tiles per request
+  const int b = (int)blockIdx.z / nz, zt = (int)blockIdx.z % nz;
+  const int pt = CAUSAL ? nz - 1 - zt : zt;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int ln = lane & 15, lg = lane >> 4;
   const int q0 = pt * (16 * QB * NW) + wave * (16 * QB);
-  const int64_t row = (int64_t)H * D;  // elements between consecutive slots
+  const int64_t row = (int64_t)H * D;  // elements between consecutive slots (key/value heads)
+  const int G = bt.G, PQ = P * G, Hq = H * G;
+  k += b * bt.kv_stride;
+  v += b * bt.kv_stride;
 
   // Q fragments (B operand of S^T = K Q^T): lane (query ln, group lg) holds
   // dims kc*32 + 8*lg .. +8 of its query.  Padding queries are zero.  Their
@@ -169,13 +180,14 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int p = q0 + qb * 16 + ln;
-    const int pc = min(p, P - 1);  // in-bounds row for padding lanes (zeroed below)
+    const int pc = min(p, PQ - 1);  // in-bounds row for padding lanes (zeroed below)
+    const int64_t qrow = (int64_t)(b * P + pc / G) * Hq + h * G + pc % G;
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc)
-      qw[qb][kc] = *reinterpret_cast<const u32x4*>(q + ((int64_t)pc * H + h) * D + kc * 32 + lg * 8);
+      qw[qb][kc] = *reinterpret_cast<const u32x4*>(q + qrow * D + kc * 32 + lg * 8);
   }
 
-  int L = (int)min<int64_t>(load_doc_len(plan), seq_len);  // a plan never exceeds the slots given
+  int L = (int)min<int64_t>(load_doc_len(plan + b), seq_len);  // a plan never exceeds the slots given
   if constexpr (CAUSAL) L = min(L, (pt + 1) * (16 * QB * NW));
   // floor(i * n_tiles / n_splits) as i * (n / k) + i * (n % k) / k: 32-bit
   // arithmetic only (i <= n_splits <= 256)
@@ -201,7 +213,7 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
   bf16x8 qf[QB][KC];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const bool pad = q0 + qb * 16 + ln >= P;
+    const bool pad = q0 + qb * 16 + ln >= PQ;
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
       const u32x4 w = pad ? u32x4{0u, 0u, 0u, 0u} : (qw[qb][kc] ^ qsign);
@@ -571,8 +583,8 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
   for (int qb = 0; qb < QB; ++qb) {
     const float lt = lsum[qb][0];
     const int p = q0 + qb * 16 + ln;
-    if (p < P) {
-      const int64_t sh = ((int64_t)split * P + p) * H + h;
+    if (p < PQ) {
+      const int64_t sh = ((int64_t)split * bt.B * P + b * P + p / G) * Hq + h * G + p % G;
       // reference of the split's state: 0 in the fast pass, the running
       // maximum in the exact pass; an empty split has none (-inf)
       const float mref = t0 >= t1 ? -INFINITY : (exact ? m[qb] : 0.f);
@@ -594,14 +606,19 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kDocThreads) void doc_valu_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v, int P, int H, float c,
     const int32_t* __restrict__ plan, int64_t seq_len, int n_splits, float* __restrict__ part_o,
-    float2* __restrict__ part_ml) {
+    float2* __restrict__ part_ml, Batch bt) {
   __shared__ __attribute__((aligned(16))) float lk[kF32NK][D];
   __shared__ __attribute__((aligned(16))) float lv[kF32NK][D];
   const int split = blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x;
-  const int pt = CAUSAL ? (int)gridDim.z - 1 - (int)blockIdx.z : (int)blockIdx.z;
-  const int p = pt * kDocThreads + tid;
-  int L = (int)min<int64_t>(load_doc_len(plan), seq_len);  // a plan never exceeds the slots given
+  const int nz = (int)gridDim.z / bt.B;  // query tiles per request (as in doc_mfma_bf16_kernel)
+  const int b = (int)blockIdx.z / nz, zt = (int)blockIdx.z % nz;
+  const int pt = CAUSAL ? nz - 1 - zt : zt;
+  const int p = pt * kDocThreads + tid;  // query s * G + g of key/value head h
+  const int G = bt.G, PQ = P * G, Hq = H * G;
+  k += b * bt.kv_stride;
+  v += b * bt.kv_stride;
+  int L = (int)min<int64_t>(load_doc_len(plan + b), seq_len);  // a plan never exceeds the slots given
   if constexpr (CAUSAL) L = min(L, (pt + 1) * kDocThreads);  // see doc_mfma_bf16_kernel
   const int n_tiles = (L + kF32NK - 1) / kF32NK;
   const int t0 = (int)((int64_t)split * n_tiles / n_splits);
@@ -612,7 +629,7 @@ __global__ __launch_bounds__(kDocThreads) void doc_valu_f32_kernel(
   float qv[D], acc[D];
 #pragma unroll
   for (int e = 0; e < D; ++e) {
-    qv[e] = p < P ? q[((int64_t)p * H + h) * D + e] : 0.f;
+    qv[e] = p < PQ ? q[((int64_t)(b * P + p / G) * Hq + h * G + p % G) * D + e] : 0.f;
     acc[e] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
@@ -656,8 +673,8 @@ __global__ __launch_bounds__(kDocThreads) void doc_valu_f32_kernel(
     }
     __syncthreads();
   }
-  if (p < P) {
-    const int64_t sh = ((int64_t)split * P + p) * H + h;
+  if (p < PQ) {
+    const int64_t sh = ((int64_t)split * bt.B * P + b * P + p / G) * Hq + h * G + p % G;
     part_ml[sh] = make_float2(m, l);
 #pragma unroll
     for (int e = 0; e < D; e += 4)
@@ -700,17 +717,18 @@ int doc_query_tile(const DocPlan& pl, pp_dtype_t dtype) {
 }
 
 hipError_t launch_doc(const DocPlan& pl, const void* q, const void* k, const void* v, int64_t seq_len, int P, int H,
-                      int d, pp_dtype_t dtype, float c, const Workspace& ws, hipStream_t stream, bool causal) {
-  const dim3 grid(pl.n_splits, H, pl.n_ptiles);
+                      int d, pp_dtype_t dtype, float c, const Workspace& ws, hipStream_t stream, bool causal,
+                      const Batch& bt) {
+  const dim3 grid(pl.n_splits, H, pl.n_ptiles * bt.B);
   if (dtype == PP_BF16) {
     auto* qq = static_cast<const uint16_t*>(q);
     auto* kk = static_cast<const uint16_t*>(k);
     auto* vv = static_cast<const uint16_t*>(v);
 #define PP_DOC_LAUNCH(DD, QQ, WW)                                                                           \
   (causal ? doc_mfma_bf16_kernel<DD, QQ, WW, true><<<grid, 64 * WW, 0, stream>>>(                                 \
-                qq, kk, vv, P, H, c, ws.plan, seq_len, pl.n_splits, ws.part_o, ws.part_ml)                        \
+                qq, kk, vv, P, H, c, ws.plan, seq_len, pl.n_splits, ws.part_o, ws.part_ml, bt)                    \
           : doc_mfma_bf16_kernel<DD, QQ, WW, false><<<grid, 64 * WW, 0, stream>>>(                                \
-                qq, kk, vv, P, H, c, ws.plan, seq_len, pl.n_splits, ws.part_o, ws.part_ml))
+                qq, kk, vv, P, H, c, ws.plan, seq_len, pl.n_splits, ws.part_o, ws.part_ml, bt))
     // dispatch on the exact (d, 16-query blocks per wave, waves) triple
     const int cfg = d * 10000 + pl.qb * 100 + pl.nw;
     switch (cfg) {
@@ -728,7 +746,7 @@ hipError_t launch_doc(const DocPlan& pl, const void* q, const void* k, const voi
     auto* kk = static_cast<const float*>(k);
     auto* vv = static_cast<const float*>(v);
 #define PP_F32_LAUNCH(DD, CC) \
-  doc_valu_f32_kernel<DD, CC><<<grid, kDocThreads, 0, stream>>>(qq, kk, vv, P, H, c, ws.plan, seq_len, pl.n_splits, ws.part_o, ws.part_ml)
+  doc_valu_f32_kernel<DD, CC><<<grid, kDocThreads, 0, stream>>>(qq, kk, vv, P, H, c, ws.plan, seq_len, pl.n_splits, ws.part_o, ws.part_ml, bt)
     if (d == 128) {
       if (causal) PP_F32_LAUNCH(128, true);
       else PP_F32_LAUNCH(128, false);

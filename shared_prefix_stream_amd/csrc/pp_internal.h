@@ -24,8 +24,31 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
+// A launch over B independent requests (each its own document, streams,
+// ids and caches, laid out one after another) whose Hq query heads share
+// Hkv = Hq / G key/value heads: query head hq reads key/value head hq / G.
+// The single-request, one-head-per-key step is B = 1, G = 1.  Stream s of
+// request b is stream b * P + s of the launch (q, out, counts, lists and
+// partials are indexed that way).
+struct Batch {
+  int B = 1;
+  int G = 1;
+  int64_t kv_stride = 0;               // elements between requests' K (and V) caches
+  int64_t id_stride = 0;               // ids between requests' stream_id arrays
+  const int32_t* seq_lens = nullptr;   // per-request lengths on the device (else seq_len for all)
+};
+
+// Length of request b's sequence: its device value clamped to [0, bound],
+// or the host value when there is none.
+__device__ __forceinline__ int64_t request_len(const Batch& bt, int b, int64_t bound) {
+  if (!bt.seq_lens) return bound;
+  const int64_t n = __builtin_amdgcn_readfirstlane(bt.seq_lens[b]);
+  return n < 0 ? 0 : (n > bound ? bound : n);
+}
+
 // Workspace layout (byte offsets from a 256-byte aligned base):
-//   [0, 256)          int32 plan[0] = doc_len (length of the leading id-0 run)
+//   [0, PL)           int32 plan[b] = doc_len of request b (length of its
+//                     leading id-0 run); PL = 256 bytes, more for B > 64
 //   [256, +CNT)       int32 counts[P]: visible slots past the prefix, per stream
 //   [.., +SL)         int32 slots[P][cap]: their ascending slot indices (the
 //                     first cap of them; a stream with more gathers them itself;
@@ -57,21 +80,25 @@ inline int64_t list_cap_for(int64_t seq_len) {
   return (c + 3) & ~(int64_t)3;
 }
 
-inline size_t workspace_bytes_for(int n_splits, int64_t P, int64_t H, int64_t d, int64_t seq_len) {
+inline size_t plan_bytes_for(int64_t B) { return align_up((size_t)(B < 2 ? 2 : B) * 4, 256); }
+
+// P: streams of the launch (all requests), H: query heads.
+inline size_t workspace_bytes_for(int n_splits, int64_t P, int64_t H, int64_t d, int64_t seq_len, int64_t B = 1) {
   const size_t cnt = align_up((size_t)P * 4, 256);
   const size_t sl = align_up((size_t)P * list_cap_for(seq_len) * 4, 256);
   const size_t ml = align_up((size_t)n_splits * P * H * sizeof(float2), 256);
   const size_t o = align_up((size_t)n_splits * P * H * d * sizeof(float), 256);
   const size_t qr = align_up((size_t)P * H * d * 4, 256);
-  return 256 /*base alignment slack*/ + 256 /*plan*/ + cnt + sl + ml + o + qr;
+  return 256 /*base alignment slack*/ + plan_bytes_for(B) + cnt + sl + ml + o + qr;
 }
 
-inline Workspace carve_workspace(void* ws, int n_splits, int64_t P, int64_t H, int64_t d, int64_t seq_len) {
+inline Workspace carve_workspace(void* ws, int n_splits, int64_t P, int64_t H, int64_t d, int64_t seq_len,
+                                 int64_t B = 1) {
   uintptr_t at = align_up((uintptr_t)ws, 256);
   Workspace w;
   w.cap = list_cap_for(seq_len);
   w.plan = reinterpret_cast<int32_t*>(at);
-  at += 256;
+  at += plan_bytes_for(B);
   w.counts = reinterpret_cast<int32_t*>(at);
   at += align_up((size_t)P * 4, 256);
   w.slots = reinterpret_cast<int32_t*>(at);
@@ -259,7 +286,7 @@ __device__ int collect_visible(const int32_t* __restrict__ sid, int64_t from, in
 // slots j in [doc_len, seq_len) it sees (counts[s]) and the first cap of
 // them in ascending order (slots[s*cap ...]).  One workgroup per stream.
 hipError_t launch_plan(const int32_t* sid, int64_t seq_len, int P, int32_t* plan, int32_t* counts, int32_t* slots,
-                       int64_t cap, hipStream_t stream);
+                       int64_t cap, hipStream_t stream, const Batch& bt = Batch());
 
 // The same for a decode step that appends one slot per stream: the step
 // starts at *base_len (device), stream s's new slot is *base_len + s and gets
@@ -291,22 +318,26 @@ DocPlan choose_doc_plan(int64_t seq_len, int P, int H, int d, pp_dtype_t dtype, 
 int doc_query_tile(const DocPlan& plan, pp_dtype_t dtype);
 // causal: prefill -- query i is slot i and query tile pt sees the document
 // slots j < min((pt + 1) * tile, doc_len) with j <= i (one split).
+// (P: streams per request, H: key/value heads; the grid covers bt.B requests)
 hipError_t launch_doc(const DocPlan& plan, const void* q, const void* k, const void* v, int64_t seq_len, int P,
                       int H, int d, pp_dtype_t dtype, float scale_log2, const Workspace& ws, hipStream_t stream,
-                      bool causal = false);
+                      bool causal = false, const Batch& bt = Batch());
 
 // Per-question document part (the "batched requests" baseline): every
 // stream reads the document itself.
 int choose_batched_splits(int64_t seq_len, int P, int H, int num_cus);
+// (P: streams per request, H: query heads)
 hipError_t launch_batched_doc(int n_splits, const void* q, const void* k, const void* v, int64_t seq_len, int P,
                               int H, int d, pp_dtype_t dtype, float scale_log2, const Workspace& ws,
-                              hipStream_t stream);
+                              hipStream_t stream, const Batch& bt = Batch());
 
 // Own-slot gather for every stream, then the fixed-order merge of the doc
 // partials and the stream's own partial; writes out.
+// (P: streams per request, H: query heads)
 hipError_t launch_tail_merge(int n_splits, const void* q, const void* k, const void* v,
                              const int32_t* sid, int64_t seq_len, int P, int H, int d, pp_dtype_t dtype,
-                             float scale_log2, const Workspace& ws, void* out, hipStream_t stream);
+                             float scale_log2, const Workspace& ws, void* out, hipStream_t stream,
+                             const Batch& bt = Batch());
 
 // Prefill: for every query slot i < seq_len, the visible slots the
 // document kernel (causal, query tile `tile`) left out -- j in

@@ -38,29 +38,39 @@ constexpr int64_t kPlanChunk = kPlanWaveSpan * kPlanNW;          // 32K slots pe
 // memory holds (other workgroups may be writing them), workgroup s stores
 // its own, and plan[1] = seq_len.  A base outside [0, limit - P] gives an
 // empty plan (plan[0] = plan[1] = 0, no counts, nothing written).
+//
+// Several requests (grid.y = B, single-request layout otherwise): workgroup
+// (s, b) plans stream s of request b over that request's ids and length;
+// plan[b] is its document length, its counts and lists are those of launch
+// stream b * P + s.
 template <bool APPEND>
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ sid, int64_t seq_len,
                                                             int32_t* __restrict__ plan, int32_t* __restrict__ counts,
                                                             int32_t* __restrict__ slots, int64_t cap,
-                                                            int32_t* sid_out, const int32_t* base_len) {
+                                                            int32_t* sid_out, const int32_t* base_len, Batch bt) {
   __shared__ int found;
   __shared__ int wsum[kPlanNW];
-  const int s = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int b = blockIdx.y;
+  const int s = blockIdx.x;                     // stream within the request
+  const int sl = b * (int)gridDim.x + s;        // stream of the launch
+  sid += b * bt.id_stride;
+  if constexpr (!APPEND) seq_len = request_len(bt, b, seq_len);
   const int s1 = s + 1;
   const uint64_t below = (1ull << lane) - 1ull;  // lanes before this one
   int64_t app = seq_len;  // first appended slot
   if constexpr (APPEND) {
-    const int64_t b = __builtin_amdgcn_readfirstlane(base_len[0]);
+    const int64_t bb = __builtin_amdgcn_readfirstlane(base_len[0]);
     const int64_t P = gridDim.x;
-    if (b < 0 || b > seq_len - P) {
+    if (bb < 0 || bb > seq_len - P) {
       if (tid == 0) {
         counts[s] = 0;
         if (s == 0) plan[0] = plan[1] = 0;
       }
       return;
     }
-    app = b;
-    seq_len = b + P;
+    app = bb;
+    seq_len = bb + P;
   }
   if (tid == 0) found = 0x7fffffff;
   __syncthreads();
@@ -149,7 +159,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
         for (int e = 0; e < 4; ++e) {
           if ((m[g] >> e) & 1u) {
             const int64_t pos = total + before + rank;
-            if (pos < cap) slots[(int64_t)s * cap + pos] = (int32_t)(wb + 4 * (64 * g + lane) + e);
+            if (pos < cap) slots[(int64_t)sl * cap + pos] = (int32_t)(wb + 4 * (64 * g + lane) + e);
             ++rank;
           }
         }
@@ -161,8 +171,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     if (cb + kPlanChunk < seq_len) __syncthreads();
   }
   if (tid == 0) {
-    counts[s] = (int32_t)total;
-    if (s == 0) plan[0] = (int32_t)(doc_len < 0 ? seq_len : doc_len);
+    counts[sl] = (int32_t)total;
+    if (s == 0) plan[b] = (int32_t)(doc_len < 0 ? seq_len : doc_len);
     if constexpr (APPEND) {
       sid_out[app + s] = s1;
       if (s == 0) plan[1] = (int32_t)seq_len;
@@ -173,14 +183,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
 }  // namespace
 
 hipError_t launch_plan(const int32_t* sid, int64_t seq_len, int P, int32_t* plan, int32_t* counts, int32_t* slots,
-                       int64_t cap, hipStream_t stream) {
-  plan_kernel<false><<<P, kPlanThreads, 0, stream>>>(sid, seq_len, plan, counts, slots, cap, nullptr, nullptr);
+                       int64_t cap, hipStream_t stream, const Batch& bt) {
+  plan_kernel<false><<<dim3(P, bt.B), kPlanThreads, 0, stream>>>(sid, seq_len, plan, counts, slots, cap, nullptr,
+                                                                 nullptr, bt);
   return hipGetLastError();
 }
 
 hipError_t launch_plan_append(int32_t* sid, const int32_t* base_len, int64_t max_len, int P, int32_t* plan,
                               int32_t* counts, int32_t* slots, int64_t cap, hipStream_t stream) {
-  plan_kernel<true><<<P, kPlanThreads, 0, stream>>>(sid, max_len, plan, counts, slots, cap, sid, base_len);
+  plan_kernel<true><<<P, kPlanThreads, 0, stream>>>(sid, max_len, plan, counts, slots, cap, sid, base_len, Batch());
   return hipGetLastError();
 }
 

@@ -94,7 +94,8 @@ __global__ __launch_bounds__(kTailThreads, 4) void tail_merge_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ sid,
     int64_t seq_len, int P, int H, float c, const int32_t* __restrict__ plan, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ slots, int64_t cap, int n_splits, const float* __restrict__ part_o,
-    const float2* __restrict__ part_ml, T* __restrict__ out, const int32_t* __restrict__ dyn_len, int tile) {
+    const float2* __restrict__ part_ml, T* __restrict__ out, const int32_t* __restrict__ dyn_len, int tile,
+    Batch bt) {
   using S = TailShape<T, D>;
   constexpr int VEC = S::VEC, LPH = S::LPH, HPI = S::HPI, GW = S::GW;
   constexpr int RED = kTailNI * (VEC + 2);  // floats per lane in the substream merge
@@ -103,10 +104,19 @@ __global__ __launch_bounds__(kTailThreads, 4) void tail_merge_kernel(
   __shared__ int scan[kTailNTS + 2];
   __shared__ float red[(kTailNTS - 1) * RED * 64];
 
+  // s: stream of the launch; sr: the same stream within its request b
+  // (several requests: each has its own ids, caches and document length;
+  // grouped key/value heads: query head h reads key/value head h / G)
   const int s = blockIdx.x, hg = blockIdx.y;
+  const int b = PREFILL ? 0 : s / P, sr = PREFILL ? s : s % P;
+  const int Pt = PREFILL ? P : P * bt.B;
+  sid += b * bt.id_stride;
+  k += b * bt.kv_stride;
+  v += b * bt.kv_stride;
+  plan += b;
   // (the substream index is wave-uniform; readfirstlane lets the compiler know)
   const int tid = threadIdx.x, ts = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int64_t row = (int64_t)H * D;
+  const int64_t row = (int64_t)(H / bt.G) * D;  // key/value heads
 
   // lane covers head head[i], dims d0[i] .. +VEC of its 16-byte vector i;
   // lanes of heads past H use head 0 for their (unconditional) loads and
@@ -143,7 +153,7 @@ __global__ __launch_bounds__(kTailThreads, 4) void tail_merge_kernel(
       const int sp = spb < n_splits ? spb : 0;
 #pragma unroll
       for (int i = 0; i < kTailNI; ++i) {
-        const int64_t sh = ((int64_t)sp * P + s) * H + safe_head[i];
+        const int64_t sh = ((int64_t)sp * Pt + s) * H + safe_head[i];
         ml[b][i] = part_ml[sh];
         const float* src = part_o + sh * D + d0[i];
 #pragma unroll
@@ -175,7 +185,7 @@ __global__ __launch_bounds__(kTailThreads, 4) void tail_merge_kernel(
         const int j = lst[min(base + u, n - 1)];
 #pragma unroll
         for (int i = 0; i < kTailNI; ++i) {
-          const int64_t off = (int64_t)j * row + (int64_t)safe_head[i] * D + d0[i];
+          const int64_t off = (int64_t)j * row + (int64_t)(safe_head[i] / bt.G) * D + d0[i];
           kr[u][i] = *reinterpret_cast<const u32x4*>(k + off);
           vr[u][i] = *reinterpret_cast<const u32x4*>(v + off);
         }
@@ -223,11 +233,12 @@ __global__ __launch_bounds__(kTailThreads, 4) void tail_merge_kernel(
   } else {
     // list longer than the plan kept: compact it here, chunk by chunk
     // (an appending step's length is on the device; seq_len bounds it)
-    const int64_t len = dyn_len ? min<int64_t>(__builtin_amdgcn_readfirstlane(dyn_len[0]), seq_len) : seq_len;
+    const int64_t len = dyn_len ? min<int64_t>(__builtin_amdgcn_readfirstlane(dyn_len[0]), seq_len)
+                                : request_len(bt, b, seq_len);
     int64_t from = load_doc_len(plan);
     while (from < len) {
       int64_t next;
-      const int n = collect_visible<kTailThreads, kTailScanU>(sid, from, len, s + 1, list, kTailCap, &next, scan);
+      const int n = collect_visible<kTailThreads, kTailScanU>(sid, from, len, sr + 1, list, kTailCap, &next, scan);
       gather(list, n);
       from = next;
       __syncthreads();  // list[] is refilled by the next round
@@ -275,12 +286,12 @@ __global__ __launch_bounds__(kTailThreads, 4) void tail_merge_kernel(
 template <typename T, int D, bool PREFILL = false>
 hipError_t launch_tail_t(int n_splits, const void* q, const void* k, const void* v, const int32_t* sid,
                          int64_t seq_len, int P, int H, float c, const Workspace& ws, void* out, hipStream_t stream,
-                         int tile = 0) {
+                         int tile = 0, const Batch& bt = Batch()) {
   using S = TailShape<T, D>;
-  const dim3 grid(P, (H + S::GW - 1) / S::GW);
+  const dim3 grid(P * bt.B, (H + S::GW - 1) / S::GW);
   tail_merge_kernel<T, D, PREFILL><<<grid, kTailThreads, 0, stream>>>(
       static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), sid, seq_len, P, H, c, ws.plan,
-      ws.counts, ws.slots, ws.cap, n_splits, ws.part_o, ws.part_ml, static_cast<T*>(out), ws.dyn_len, tile);
+      ws.counts, ws.slots, ws.cap, n_splits, ws.part_o, ws.part_ml, static_cast<T*>(out), ws.dyn_len, tile, bt);
   return hipGetLastError();
 }
 
@@ -288,12 +299,12 @@ hipError_t launch_tail_t(int n_splits, const void* q, const void* k, const void*
 
 hipError_t launch_tail_merge(int n_splits, const void* q, const void* k, const void* v, const int32_t* sid,
                              int64_t seq_len, int P, int H, int d, pp_dtype_t dtype, float c, const Workspace& ws,
-                             void* out, hipStream_t stream) {
+                             void* out, hipStream_t stream, const Batch& bt) {
   if (dtype == PP_BF16)
-    return d == 128 ? launch_tail_t<uint16_t, 128>(n_splits, q, k, v, sid, seq_len, P, H, c, ws, out, stream)
-                    : launch_tail_t<uint16_t, 64>(n_splits, q, k, v, sid, seq_len, P, H, c, ws, out, stream);
-  return d == 128 ? launch_tail_t<float, 128>(n_splits, q, k, v, sid, seq_len, P, H, c, ws, out, stream)
-                  : launch_tail_t<float, 64>(n_splits, q, k, v, sid, seq_len, P, H, c, ws, out, stream);
+    return d == 128 ? launch_tail_t<uint16_t, 128>(n_splits, q, k, v, sid, seq_len, P, H, c, ws, out, stream, 0, bt)
+                    : launch_tail_t<uint16_t, 64>(n_splits, q, k, v, sid, seq_len, P, H, c, ws, out, stream, 0, bt);
+  return d == 128 ? launch_tail_t<float, 128>(n_splits, q, k, v, sid, seq_len, P, H, c, ws, out, stream, 0, bt)
+                  : launch_tail_t<float, 64>(n_splits, q, k, v, sid, seq_len, P, H, c, ws, out, stream, 0, bt);
 }
 
 hipError_t launch_prefill_rest(int n_splits, int tile, const void* q, const void* k, const void* v,

@@ -27,7 +27,8 @@ def test_library_exports_every_declared_function():
     names = _declared_functions()
     assert set(names) >= {"pp_attn_decode", "pp_attn_decode_batched", "pp_attn_workspace_bytes", "pp_attn_plan",
                           "pp_attn_decode_planned", "pp_step_plan", "pp_attn_decode_append",
-                          "pp_attn_prefill", "pp_attn_prefill_workspace_bytes", "pp_abi_version", "pp_status_string", "pp_last_error_message"}
+                          "pp_attn_prefill", "pp_attn_prefill_workspace_bytes", "pp_attn_decode_multi",
+                          "pp_attn_decode_multi_batched", "pp_attn_multi_workspace_bytes", "pp_abi_version", "pp_status_string", "pp_last_error_message"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in ppattn.h but not exported"
 
@@ -216,6 +217,30 @@ def test_prefill_validation():
     assert call(ws=Q + 4096) == pp.PP_ERR_INVALID_ARG         # workspace overlaps q
     assert call(wsb=n - 1) == pp.PP_ERR_WORKSPACE
     assert call(ws=None) == pp.PP_ERR_WORKSPACE
+    assert lib.pp_last_error_message().decode() != ""
+
+
+def test_multi_validation():
+    lib = pp.raw()
+    LENS = 0x70000000
+    assert lib.pp_attn_multi_workspace_bytes(1000, 3, 8, 8, 3, 128, pp.PP_BF16) == 0  # 8 % 3 != 0
+    assert lib.pp_attn_multi_workspace_bytes(1000, 0, 8, 8, 2, 128, pp.PP_BF16) == 0
+    n = lib.pp_attn_multi_workspace_bytes(1000, 3, 8, 8, 2, 128, pp.PP_BF16)
+    assert n >= 3 * 8 * 8 * (128 + 2) * 4
+    assert n > lib.pp_attn_multi_workspace_bytes(1000, 1, 8, 8, 2, 128, pp.PP_BF16)
+
+    def call(B=3, Hq=8, Hkv=2, lens=LENS, out=OUT, wsb=n, batched=False):
+        fn = lib.pp_attn_decode_multi_batched if batched else lib.pp_attn_decode_multi
+        return fn(Q, K, V, SID, lens, 1000, B, 8, Hq, Hkv, 128, 0.088, out, pp.PP_BF16, WS, wsb, None)
+
+    assert call(B=0) == pp.PP_ERR_INVALID_ARG
+    assert call(Hkv=3) == pp.PP_ERR_INVALID_ARG
+    assert call(Hkv=0) == pp.PP_ERR_INVALID_ARG
+    assert call(lens=None) == pp.PP_ERR_INVALID_ARG
+    assert call(lens=OUT + 64) == pp.PP_ERR_INVALID_ARG        # lengths inside out
+    assert call(out=K + 3 * 1000 * 2 * 128 * 2 - 64) == pp.PP_ERR_INVALID_ARG  # out overlaps the last request's keys
+    assert call(wsb=n - 1) == pp.PP_ERR_WORKSPACE
+    assert call(wsb=n - 1, batched=True) == pp.PP_ERR_WORKSPACE
     assert lib.pp_last_error_message().decode() != ""
 
 

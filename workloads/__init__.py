@@ -45,6 +45,8 @@ __all__ = [
     "PrefillCase",
     "prefill_case",
     "prefill_doc16k_p256",
+    "MultiCase",
+    "multi_case",
 ]
 
 
@@ -219,6 +221,49 @@ def long_answer_case(answer_len: int, seed: int, doc_len: int = 8192, P: int = 1
     rng = np.random.Generator(np.random.PCG64(seed ^ 0x10A6))
     return make_case(H, D, doc_len, _uniform_ints(rng, 16, 32, P), [answer_len] * P, dtype=torch.bfloat16,
                      seed=seed, name=f"codellama7b_doc{doc_len // 1024}k_p{P}_answers{answer_len}")
+
+
+@dataclasses.dataclass
+class MultiCase:
+    q: torch.Tensor          # [B, P, Hq, D]
+    k: torch.Tensor          # [B, T, Hkv, D]
+    v: torch.Tensor
+    stream_id: torch.Tensor  # [B, T] int32
+    seq_lens: List[int]      # per request
+    doc_lens: List[int]
+    P: int
+    Hq: int
+    Hkv: int
+    D: int
+    scale: float
+    name: str
+
+
+def multi_case(Hq: int, Hkv: int, D: int, P: int, doc_lens: Sequence[int], q_range=(8, 48), a_len: int = 31,
+               dtype: torch.dtype = torch.bfloat16, seed: int = 0, name: str = "") -> MultiCase:
+    """B = len(doc_lens) independent requests, each its own document and P
+    streams (questions uniform in q_range, a_len prior answer tokens), laid
+    out one after another with room for the longest; rows past a request's
+    length hold NaN (nothing may read them) and junk ids."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    layouts = []
+    for dl in doc_lens:
+        ids, _ = canonical_layout(int(dl), _uniform_ints(rng, q_range[0], q_range[1], P), [a_len] * P)
+        layouts.append(ids)
+    T = max(len(x) for x in layouts)
+    B = len(doc_lens)
+    sid = np.full((B, T), -5, dtype=np.int32)
+    for b, ids in enumerate(layouts):
+        sid[b, : len(ids)] = ids
+    q = rng.standard_normal((B, P, Hq, D), dtype=np.float32)
+    k = rng.standard_normal((B, T, Hkv, D), dtype=np.float32)
+    v = rng.standard_normal((B, T, Hkv, D), dtype=np.float32)
+    for b, ids in enumerate(layouts):
+        k[b, len(ids):] = np.nan
+        v[b, len(ids):] = np.nan
+    return MultiCase(q=_round(q, dtype), k=_round(k, dtype), v=_round(v, dtype), stream_id=torch.from_numpy(sid),
+                     seq_lens=[len(x) for x in layouts], doc_lens=[int(x) for x in doc_lens], P=P, Hq=Hq, Hkv=Hkv,
+                     D=D, scale=1.0 / math.sqrt(D), name=name)
 
 
 @dataclasses.dataclass
