@@ -310,6 +310,60 @@ def prefill_bench(torch, pp, dev, doc=16384, P=256, H=32, D=128, seed=1006, runs
             "mfma_frac": flops / (ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
 
 
+def multi_bench(torch, pp, dev, B=4, P=64, Hq=28, Hkv=4, D=128, doc=16384, a_len=31, seed=1007, steps=20):
+    """Several requests per launch with grouped key/value heads: 4 requests of
+    64 streams (the pages' best streams per request is 16-64), each on its
+    own 16k-token document, 28 query heads sharing 4 key/value heads (the
+    pages' real-benchmark model family); one decode step, and the
+    per-question baseline on the same inputs."""
+    import numpy as np
+
+    from workloads import _uniform_ints, canonical_layout
+
+    rng = np.random.Generator(np.random.PCG64(seed))
+    layouts, q_total = [], 0
+    for _ in range(B):
+        ql = _uniform_ints(rng, 8, 48, P)
+        q_total += sum(ql)
+        layouts.append(canonical_layout(doc, ql, [a_len] * P)[0])
+    T = max(len(x) for x in layouts)
+    sid_np = np.full((B, T), -5, dtype=np.int32)
+    for b, ids in enumerate(layouts):
+        sid_np[b, : len(ids)] = ids
+    g = torch.Generator(device=dev).manual_seed(seed)
+    q = torch.randn(B, P, Hq, D, generator=g, device=dev, dtype=torch.bfloat16)
+    k = torch.randn(B, T, Hkv, D, generator=g, device=dev, dtype=torch.bfloat16)
+    v = torch.randn(B, T, Hkv, D, generator=g, device=dev, dtype=torch.bfloat16)
+    sid = torch.from_numpy(sid_np).to(dev)
+    lens = torch.tensor([len(x) for x in layouts], dtype=torch.int32, device=dev)
+    out = torch.empty_like(q)
+    ws = torch.empty(pp.multi_workspace_bytes(T, B, P, Hq, Hkv, D, torch.bfloat16), dtype=torch.uint8, device=dev)
+
+    def t(batched, n):
+        for _ in range(2):
+            pp.pp_attn_decode_multi(q, k, v, sid, lens, out=out, workspace=ws, batched=batched)
+        torch.cuda.synchronize()
+        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            pp.pp_attn_decode_multi(q, k, v, sid, lens, out=out, workspace=ws, batched=batched)
+        e.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(e) / n
+
+    ms = t(False, steps)
+    bms = t(True, max(3, steps // 4))
+    slot_bytes = Hkv * D * 2 * 2  # K + V of one slot, all key/value heads
+    kv = (B * doc + q_total + B * P * a_len) * slot_bytes
+    return {"workload": f"qwen2.5-7b-heads_{B}x{P}streams_doc16k", "B": B, "P": P, "Hq": Hq, "Hkv": Hkv, "d": D,
+            "doc_len": doc, "questions": "uniform 8-48", "answers": a_len, "ms_per_step": ms,
+            "answer_tok_s": B * P / (ms / 1e3), "effective_kv_gbs": kv / (ms / 1e3) / 1e9,
+            "effective_kv_hbm_frac": kv / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "tflops": 4 * D * Hq * B * P * doc / (ms / 1e3) / 1e12,
+            "mfma_frac": 4 * D * Hq * B * P * doc / (ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "batched_baseline_ms": bms, "speedup_of_decode": bms / ms}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -330,6 +384,8 @@ def main():
                     help="skip the long-answer sweep (8k document, 128 streams, 128-1024 answer tokens)")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the prefill of the 16k-token document with 256 questions")
+    ap.add_argument("--no-multi", action="store_true",
+                    help="skip the 4-request, grouped-head (28/4) decode step")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -471,6 +527,12 @@ def main():
         prefill = prefill_bench(torch, pp, dev)
         torch.cuda.empty_cache()
 
+    multi = None
+    if not args.no_multi:
+        log("bench: several requests, grouped heads")
+        multi = multi_bench(torch, pp, dev)
+        torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: CPU oracle baseline")
@@ -507,6 +569,7 @@ def main():
         "decode_loop": loop,
         "answer_sweep": sweep,
         "prefill": prefill,
+        "multi_request_gqa": multi,
         "cpu_baseline": cpu,
         "kernel_source_digest": kernel_source_digest(),
     }
