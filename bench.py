@@ -364,6 +364,70 @@ def multi_bench(torch, pp, dev, B=4, P=64, Hq=28, Hkv=4, D=128, doc=16384, a_len
             "batched_baseline_ms": bms, "speedup_of_decode": bms / ms}
 
 
+def serving_bench(torch, pp, dev, R=16, B=4, P=16, Hq=28, Hkv=4, D=128, seed=1008):
+    """Continuous against static batching of request slots: 16 requests of
+    16 streams on 4k-8k-token documents, every other one asking for long
+    answers (128 tokens against 8), 4 slots of one pp_attn_decode_multi
+    launch per step.  Refilling a slot copies the request's cache in (a
+    stand-in for its prefill) and is inside the timed loop."""
+    import numpy as np
+
+    from shared_prefix_stream_amd.batching import continuous_schedule, static_schedule
+    from workloads import _uniform_ints, canonical_layout
+
+    answer = [8, 128] * (R // 2)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    reqs = []
+    for a in answer:
+        doc = int(rng.integers(4096, 8193))
+        ql = _uniform_ints(rng, 16, 32, P)
+        reqs.append((canonical_layout(doc, ql, [a] * P)[0], doc + sum(ql)))
+    T = max(len(ids) for ids, _ in reqs)
+    g = torch.Generator(device=dev).manual_seed(seed)
+    pool_k = [torch.randn(len(ids), Hkv, D, generator=g, device=dev, dtype=torch.bfloat16) for ids, _ in reqs]
+    pool_v = [torch.randn(len(ids), Hkv, D, generator=g, device=dev, dtype=torch.bfloat16) for ids, _ in reqs]
+    pool_ids = [torch.from_numpy(ids).to(dev) for ids, _ in reqs]
+    K = torch.zeros(B, T, Hkv, D, device=dev, dtype=torch.bfloat16)
+    V = torch.zeros_like(K)
+    sid = torch.full((B, T), -1, dtype=torch.int32, device=dev)
+    q = torch.randn(B, P, Hq, D, generator=g, device=dev, dtype=torch.bfloat16)
+    out = torch.empty_like(q)
+    ws = torch.empty(pp.multi_workspace_bytes(T, B, P, Hq, Hkv, D, torch.bfloat16), dtype=torch.uint8, device=dev)
+
+    def run(steps):
+        lens = torch.tensor([[0 if x is None else reqs[x[0]][1] + (x[1] + 1) * P for x in st] for st in steps],
+                            dtype=torch.int32, device=dev)
+        placed = [None] * B
+        torch.cuda.synchronize()
+        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i, st in enumerate(steps):
+            for b, x in enumerate(st):
+                if x is not None and placed[b] != x[0]:
+                    r = x[0]
+                    n = pool_ids[r].shape[0]
+                    K[b, :n].copy_(pool_k[r])
+                    V[b, :n].copy_(pool_v[r])
+                    sid[b, :n].copy_(pool_ids[r])
+                    placed[b] = r
+            pp.pp_attn_decode_multi(q, K, V, sid, lens[i], out=out, workspace=ws)
+        e.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(e)
+
+    res = {}
+    for name, fn in (("static", static_schedule), ("continuous", continuous_schedule)):
+        steps = fn(answer, B)
+        run(steps)  # warm-up pass
+        ms = run(steps)
+        res[name] = {"decode_steps": len(steps), "ms": ms, "answer_tok_s": P * sum(answer) / (ms / 1e3)}
+    return {"workload": f"qwen2.5-7b-heads_{R}requests_x{P}streams_{B}slots_answers8-128",
+            "requests": R, "slots": B, "P": P, "Hq": Hq, "Hkv": Hkv, "doc_len": "uniform 4096-8192",
+            "answers": "8 and 128 tokens, alternating", **res,
+            "steps_saved_frac": 1 - res["continuous"]["decode_steps"] / res["static"]["decode_steps"],
+            "speedup": res["static"]["ms"] / res["continuous"]["ms"]}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -386,6 +450,8 @@ def main():
                     help="skip the prefill of the 16k-token document with 256 questions")
     ap.add_argument("--no-multi", action="store_true",
                     help="skip the 4-request, grouped-head (28/4) decode step")
+    ap.add_argument("--no-serving", action="store_true",
+                    help="skip continuous against static batching of 16 requests in 4 slots")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -533,6 +599,12 @@ def main():
         multi = multi_bench(torch, pp, dev)
         torch.cuda.empty_cache()
 
+    serving = None
+    if not args.no_serving:
+        log("bench: continuous against static batching")
+        serving = serving_bench(torch, pp, dev)
+        torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: CPU oracle baseline")
@@ -570,6 +642,7 @@ def main():
         "answer_sweep": sweep,
         "prefill": prefill,
         "multi_request_gqa": multi,
+        "continuous_batching": serving,
         "cpu_baseline": cpu,
         "kernel_source_digest": kernel_source_digest(),
     }

@@ -161,6 +161,14 @@ pp_status_t pp_attn_decode_planned(const void* q, const void* k_cache, const voi
  *                                           s + 1 = its stream s)
  *   seq_lens   device int32[B]: request b's seq_len, clamped on the device to
  *              [0, max_seq_len] (0: its streams see nothing, out is zero)
+ *   active     device int32[B * P] or NULL (all active): 0 retires stream
+ *              b * P + s -- it sees nothing, its output is zero and its
+ *              per-stream work is skipped.
+ * A server batching continuously (project page, "Continuous batching":
+ * the batch is refilled as requests finish) keeps B request slots: a slot
+ * whose request finished gets length 0 (idle, no document work) until the
+ * next request's ids and caches are written there and its length set;
+ * streams that finished early are retired with `active`.
  * Hq must be a multiple of Hkv.  The document kernel contracts each K/V tile
  * of a request against all P * Hq / Hkv queries of its key/value head.
  * Workspace: pp_attn_multi_workspace_bytes(max_seq_len, B, P, Hq, Hkv, d,
@@ -171,15 +179,16 @@ pp_status_t pp_attn_decode_planned(const void* q, const void* k_cache, const voi
 size_t pp_attn_multi_workspace_bytes(int64_t max_seq_len, int32_t B, int32_t P, int32_t Hq, int32_t Hkv,
                                      int32_t d, pp_dtype_t dtype);
 pp_status_t pp_attn_decode_multi(const void* q, const void* k_cache, const void* v_cache,
-                                 const int32_t* stream_id, const int32_t* seq_lens, int64_t max_seq_len,
-                                 int32_t B, int32_t P, int32_t Hq, int32_t Hkv, int32_t d, float scale,
-                                 void* out, pp_dtype_t dtype, void* workspace, size_t workspace_bytes,
-                                 void* hip_stream);
+                                 const int32_t* stream_id, const int32_t* seq_lens, const int32_t* active,
+                                 int64_t max_seq_len, int32_t B, int32_t P, int32_t Hq, int32_t Hkv,
+                                 int32_t d, float scale, void* out, pp_dtype_t dtype, void* workspace,
+                                 size_t workspace_bytes, void* hip_stream);
 pp_status_t pp_attn_decode_multi_batched(const void* q, const void* k_cache, const void* v_cache,
                                          const int32_t* stream_id, const int32_t* seq_lens,
-                                         int64_t max_seq_len, int32_t B, int32_t P, int32_t Hq, int32_t Hkv,
-                                         int32_t d, float scale, void* out, pp_dtype_t dtype,
-                                         void* workspace, size_t workspace_bytes, void* hip_stream);
+                                         const int32_t* active, int64_t max_seq_len, int32_t B, int32_t P,
+                                         int32_t Hq, int32_t Hkv, int32_t d, float scale, void* out,
+                                         pp_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                         void* hip_stream);
 
 /* Starts a decode step in which every stream appends one slot (Parallel
  * Prompting project page, "How it works": each decode step appends one token

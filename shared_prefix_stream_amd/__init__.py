@@ -113,7 +113,7 @@ def _load():
     for name in ("pp_attn_decode_multi", "pp_attn_decode_multi_batched"):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
-        fn.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, f32, vp, ctypes.c_int, vp, sz, vp]
+        fn.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, f32, vp, ctypes.c_int, vp, sz, vp]
     _lib = lib
     return lib
 
@@ -417,11 +417,12 @@ def multi_workspace_bytes(max_seq_len: int, B: int, P: int, Hq: int, Hkv: int, d
 
 
 def pp_attn_decode_multi(q, k_cache, v_cache, stream_id, seq_lens, scale: Optional[float] = None, out=None,
-                         workspace=None, batched: bool = False):
+                         workspace=None, batched: bool = False, active=None):
     """B requests in one launch, grouped key/value heads: q [B, P, Hq, d],
     k_cache/v_cache [B, T, Hkv, d], stream_id [B, T] int32, seq_lens [B]
-    int32 (all on the GPU).  batched=True runs the per-question baseline.
-    Returns out [B, P, Hq, d] without synchronising."""
+    int32, optional active [B, P] int32 (0 retires a stream), all on the GPU.
+    batched=True runs the per-question baseline.  Returns out [B, P, Hq, d]
+    without synchronising."""
     import torch
 
     for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("stream_id", stream_id),
@@ -440,6 +441,10 @@ def pp_attn_decode_multi(q, k_cache, v_cache, stream_id, seq_lens, scale: Option
         raise ValueError("stream_id must be an int32 [B, T] tensor")
     if seq_lens.dtype != torch.int32 or tuple(seq_lens.shape) != (B,):
         raise ValueError("seq_lens must be an int32 [B] tensor")
+    if active is not None:
+        if (not isinstance(active, torch.Tensor) or not active.is_cuda or not active.is_contiguous()
+                or active.dtype != torch.int32 or tuple(active.shape) != (B, P)):
+            raise ValueError("active must be a contiguous int32 [B, P] GPU tensor")
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     code = _dtype_code(q.dtype)
     if out is None:
@@ -449,7 +454,8 @@ def pp_attn_decode_multi(q, k_cache, v_cache, stream_id, seq_lens, scale: Option
     if workspace is None:
         workspace = torch.empty(multi_workspace_bytes(T, B, P, Hq, Hkv, d, code), dtype=torch.uint8, device=q.device)
     fn = _load().pp_attn_decode_multi_batched if batched else _load().pp_attn_decode_multi
-    _check(fn(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), stream_id.data_ptr(), seq_lens.data_ptr(), T, B, P,
+    _check(fn(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), stream_id.data_ptr(), seq_lens.data_ptr(),
+              None if active is None else active.data_ptr(), T, B, P,
               Hq, Hkv, d, scale, out.data_ptr(), code, workspace.data_ptr(),
               workspace.numel() * workspace.element_size(), _stream_handle(q.device)))
     return out

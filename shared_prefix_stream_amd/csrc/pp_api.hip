@@ -340,9 +340,9 @@ size_t pp_attn_multi_workspace_bytes(int64_t max_seq_len, int32_t B, int32_t P, 
 }
 
 static pp_status_t multi_impl(Path path, const void* q, const void* k, const void* v, const int32_t* sid,
-                              const int32_t* seq_lens, int64_t max_seq_len, int32_t B, int32_t P, int32_t Hq,
-                              int32_t Hkv, int32_t d, float scale, void* out, pp_dtype_t dtype, void* workspace,
-                              size_t workspace_bytes, void* hip_stream) {
+                              const int32_t* seq_lens, const int32_t* active, int64_t max_seq_len, int32_t B,
+                              int32_t P, int32_t Hq, int32_t Hkv, int32_t d, float scale, void* out,
+                              pp_dtype_t dtype, void* workspace, size_t workspace_bytes, void* hip_stream) {
   if (B < 1 || B > PP_MAX_REQUESTS) return fail(PP_ERR_INVALID_ARG, "B=%d out of range [1, %d]", B, PP_MAX_REQUESTS);
   if (Hkv < 1 || Hq < 1 || Hq % Hkv != 0)
     return fail(PP_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
@@ -353,28 +353,31 @@ static pp_status_t multi_impl(Path path, const void* q, const void* k, const voi
   bt.B = B;
   bt.G = Hq / Hkv;
   bt.seq_lens = seq_lens;
+  bt.active = active;
   const size_t nq = (size_t)B * P * Hq * d * elem_size(dtype);
   if (overlaps(out, nq, seq_lens, (size_t)B * 4) || overlaps(workspace, workspace_bytes, seq_lens, (size_t)B * 4))
     return fail(PP_ERR_INVALID_ARG, "seq_lens overlaps out or the workspace");
+  if (overlaps(out, nq, active, (size_t)B * P * 4) || overlaps(workspace, workspace_bytes, active, (size_t)B * P * 4))
+    return fail(PP_ERR_INVALID_ARG, "active overlaps out or the workspace");
   return decode_impl(path, q, k, v, sid, max_seq_len, P, Hq, d, scale, out, dtype, workspace, workspace_bytes,
                      hip_stream, nullptr, nullptr, nullptr, bt);
 }
 
 pp_status_t pp_attn_decode_multi(const void* q, const void* k_cache, const void* v_cache, const int32_t* stream_id,
-                                 const int32_t* seq_lens, int64_t max_seq_len, int32_t B, int32_t P, int32_t Hq,
-                                 int32_t Hkv, int32_t d, float scale, void* out, pp_dtype_t dtype, void* workspace,
-                                 size_t workspace_bytes, void* hip_stream) {
-  return multi_impl(Path::kParallel, q, k_cache, v_cache, stream_id, seq_lens, max_seq_len, B, P, Hq, Hkv, d, scale,
-                    out, dtype, workspace, workspace_bytes, hip_stream);
+                                 const int32_t* seq_lens, const int32_t* active, int64_t max_seq_len, int32_t B,
+                                 int32_t P, int32_t Hq, int32_t Hkv, int32_t d, float scale, void* out,
+                                 pp_dtype_t dtype, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return multi_impl(Path::kParallel, q, k_cache, v_cache, stream_id, seq_lens, active, max_seq_len, B, P, Hq, Hkv, d,
+                    scale, out, dtype, workspace, workspace_bytes, hip_stream);
 }
 
 pp_status_t pp_attn_decode_multi_batched(const void* q, const void* k_cache, const void* v_cache,
-                                         const int32_t* stream_id, const int32_t* seq_lens, int64_t max_seq_len,
-                                         int32_t B, int32_t P, int32_t Hq, int32_t Hkv, int32_t d, float scale,
-                                         void* out, pp_dtype_t dtype, void* workspace, size_t workspace_bytes,
-                                         void* hip_stream) {
-  return multi_impl(Path::kBatched, q, k_cache, v_cache, stream_id, seq_lens, max_seq_len, B, P, Hq, Hkv, d, scale,
-                    out, dtype, workspace, workspace_bytes, hip_stream);
+                                         const int32_t* stream_id, const int32_t* seq_lens, const int32_t* active,
+                                         int64_t max_seq_len, int32_t B, int32_t P, int32_t Hq, int32_t Hkv,
+                                         int32_t d, float scale, void* out, pp_dtype_t dtype, void* workspace,
+                                         size_t workspace_bytes, void* hip_stream) {
+  return multi_impl(Path::kBatched, q, k_cache, v_cache, stream_id, seq_lens, active, max_seq_len, B, P, Hq, Hkv, d,
+                    scale, out, dtype, workspace, workspace_bytes, hip_stream);
 }
 
 size_t pp_attn_prefill_workspace_bytes(int64_t seq_len, int32_t H, int32_t d, pp_dtype_t dtype) {

@@ -68,6 +68,7 @@ __global__ __launch_bounds__(kBThreads) void batched_doc_kernel(
   __shared__ float red[NW][VEC + 2][LPK];
 
   const int h = blockIdx.x, split = blockIdx.y, s = blockIdx.z;  // s: stream of the launch
+  if (!stream_active(bt, s)) return;                               // retired: the merge writes zeros
   const int b = s / P;                                             // its request
   // (the wave index is wave-uniform; readfirstlane lets the compiler know)
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;

@@ -36,7 +36,12 @@ struct Batch {
   int64_t kv_stride = 0;               // elements between requests' K (and V) caches
   int64_t id_stride = 0;               // ids between requests' stream_id arrays
   const int32_t* seq_lens = nullptr;   // per-request lengths on the device (else seq_len for all)
+  const int32_t* active = nullptr;     // per launch stream: 0 = retired (sees nothing, output 0); null: all
 };
+
+__device__ __forceinline__ bool stream_active(const Batch& bt, int s) {
+  return !bt.active || __builtin_amdgcn_readfirstlane(bt.active[s]) != 0;
+}
 
 // Length of request b's sequence: its device value clamped to [0, bound],
 // or the host value when there is none.

@@ -56,6 +56,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
   const int sl = b * (int)gridDim.x + s;        // stream of the launch
   sid += b * bt.id_stride;
   if constexpr (!APPEND) seq_len = request_len(bt, b, seq_len);
+  const unsigned live = stream_active(bt, sl) ? 1u : 0u;  // a retired stream lists nothing
   const int s1 = s + 1;
   const uint64_t below = (1ull << lane) - 1ull;  // lanes before this one
   int64_t app = seq_len;  // first appended slot
@@ -131,7 +132,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * (64 * g + lane) + e;
-        const unsigned vis = (unsigned)(r >= lo) & (unsigned)(r < hi) &
+        const unsigned vis = (unsigned)(r >= lo) & (unsigned)(r < hi) & live &
                              ((unsigned)(ids[e] == 0) | (unsigned)(ids[e] == s1));
         m[g] |= vis << e;
       }

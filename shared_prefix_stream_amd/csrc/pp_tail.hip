@@ -117,6 +117,13 @@ __global__ __launch_bounds__(kTailThreads, 4) void tail_merge_kernel(
   // (the substream index is wave-uniform; readfirstlane lets the compiler know)
   const int tid = threadIdx.x, ts = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int64_t row = (int64_t)(H / bt.G) * D;  // key/value heads
+  if (!PREFILL && !stream_active(bt, s)) {  // a retired stream: zeros, no work (workgroup-uniform)
+    const int head0 = hg * S::GW;
+    const int nel = (min(H, head0 + S::GW) - head0) * D;
+    T* o = out + ((int64_t)s * H + head0) * D;
+    for (int e = tid * VEC; e < nel; e += kTailThreads * VEC) *reinterpret_cast<u32x4*>(o + e) = u32x4{0u, 0u, 0u, 0u};
+    return;
+  }
 
   // lane covers head head[i], dims d0[i] .. +VEC of its 16-byte vector i;
   // lanes of heads past H use head 0 for their (unconditional) loads and

@@ -229,9 +229,9 @@ def test_multi_validation():
     assert n >= 3 * 8 * 8 * (128 + 2) * 4
     assert n > lib.pp_attn_multi_workspace_bytes(1000, 1, 8, 8, 2, 128, pp.PP_BF16)
 
-    def call(B=3, Hq=8, Hkv=2, lens=LENS, out=OUT, wsb=n, batched=False):
+    def call(B=3, Hq=8, Hkv=2, lens=LENS, out=OUT, wsb=n, batched=False, active=None):
         fn = lib.pp_attn_decode_multi_batched if batched else lib.pp_attn_decode_multi
-        return fn(Q, K, V, SID, lens, 1000, B, 8, Hq, Hkv, 128, 0.088, out, pp.PP_BF16, WS, wsb, None)
+        return fn(Q, K, V, SID, lens, active, 1000, B, 8, Hq, Hkv, 128, 0.088, out, pp.PP_BF16, WS, wsb, None)
 
     assert call(B=0) == pp.PP_ERR_INVALID_ARG
     assert call(Hkv=3) == pp.PP_ERR_INVALID_ARG
@@ -241,6 +241,7 @@ def test_multi_validation():
     assert call(out=K + 3 * 1000 * 2 * 128 * 2 - 64) == pp.PP_ERR_INVALID_ARG  # out overlaps the last request's keys
     assert call(wsb=n - 1) == pp.PP_ERR_WORKSPACE
     assert call(wsb=n - 1, batched=True) == pp.PP_ERR_WORKSPACE
+    assert call(active=WS + 256) == pp.PP_ERR_INVALID_ARG      # stream flags inside the workspace
     assert lib.pp_last_error_message().decode() != ""
 
 

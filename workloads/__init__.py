@@ -47,6 +47,8 @@ __all__ = [
     "prefill_doc16k_p256",
     "MultiCase",
     "multi_case",
+    "ServingPool",
+    "serving_pool",
 ]
 
 
@@ -264,6 +266,47 @@ def multi_case(Hq: int, Hkv: int, D: int, P: int, doc_lens: Sequence[int], q_ran
     return MultiCase(q=_round(q, dtype), k=_round(k, dtype), v=_round(v, dtype), stream_id=torch.from_numpy(sid),
                      seq_lens=[len(x) for x in layouts], doc_lens=[int(x) for x in doc_lens], P=P, Hq=Hq, Hkv=Hkv,
                      D=D, scale=1.0 / math.sqrt(D), name=name)
+
+
+@dataclasses.dataclass
+class ServingPool:
+    """Requests waiting to be decoded, each with its own document, P streams
+    and answer length (every stream of a request answers that many tokens);
+    caches hold the document, the questions and all the answers' K/V in the
+    canonical layout, so the cache at a request's step t is its first
+    base + (t + 1) * P slots."""
+    ids: List[np.ndarray]           # per request [T_r] int32
+    k: List[torch.Tensor]           # per request [T_r, Hkv, D]
+    v: List[torch.Tensor]
+    base: List[int]                 # document + questions, per request
+    answer_lens: List[int]
+    P: int
+    Hq: int
+    Hkv: int
+    D: int
+    seed: int
+
+    def queries(self, r: int, t: int, dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+        """The P queries [P, Hq, D] of request r at its answer step t."""
+        rng = np.random.Generator(np.random.PCG64([self.seed, r, t]))
+        return _round(rng.standard_normal((self.P, self.Hq, self.D), dtype=np.float32), dtype)
+
+
+def serving_pool(answer_lens: Sequence[int], P: int, Hq: int, Hkv: int, D: int, doc_range=(64, 256),
+                 q_range=(2, 12), dtype: torch.dtype = torch.bfloat16, seed: int = 0) -> ServingPool:
+    rng = np.random.Generator(np.random.PCG64(seed))
+    ids_l, k_l, v_l, base = [], [], [], []
+    for a in answer_lens:
+        doc = int(rng.integers(doc_range[0], doc_range[1] + 1))
+        q_lens = _uniform_ints(rng, q_range[0], q_range[1], P)
+        ids, _ = canonical_layout(doc, q_lens, [int(a)] * P)
+        T = len(ids)
+        ids_l.append(ids)
+        k_l.append(_round(rng.standard_normal((T, Hkv, D), dtype=np.float32), dtype))
+        v_l.append(_round(rng.standard_normal((T, Hkv, D), dtype=np.float32), dtype))
+        base.append(doc + sum(q_lens))
+    return ServingPool(ids=ids_l, k=k_l, v=v_l, base=base, answer_lens=[int(a) for a in answer_lens], P=P, Hq=Hq,
+                       Hkv=Hkv, D=D, seed=seed)
 
 
 @dataclasses.dataclass
