@@ -559,7 +559,10 @@ def main():
     }
     kernels = {}
     for name, us in stage_us.items():
-        gbs = stage_bytes[name] / (us * 1e-6) / 1e9 if us > 0 else 0.0
+        if us < 0.5:  # the stage has no launch of its own (the plain step folds the plan into its kernels)
+            kernels[name] = {"us": us, "algorithmic_bytes": stage_bytes[name], "separate_launch": False}
+            continue
+        gbs = stage_bytes[name] / (us * 1e-6) / 1e9
         kernels[name] = {"us": us, "algorithmic_bytes": stage_bytes[name], "gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
     doc_tflops = by["doc_flops"] / (stage_us["document"] * 1e-6) / 1e12
     kernels["document"]["mfma_tflops"] = doc_tflops
