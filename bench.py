@@ -129,6 +129,22 @@ def cpu_baseline(case, target_s: float):
     }
 
 
+def _blas_threads() -> int:
+    from threadpoolctl import threadpool_info
+
+    return int(max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1]))
+
+
+def oracle_rate(fn, units: float, unit: str, sample: str):
+    """Time one call of an oracle function on a bounded sample: `units` of
+    `unit` done in that call -> rate (the oracle as it stands, CPU only)."""
+    t = time.perf_counter()
+    fn()
+    dt = time.perf_counter() - t
+    return {"value": units / dt, "unit": unit, "cores": _blas_threads(), "kind": "oracle",
+            "sample": f"{sample}, fp64 NumPy, {dt:.1f} s", "seconds": dt}
+
+
 def _cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -157,7 +173,8 @@ def copy_calibration(steps: int):
                       "gbs_read_plus_write": 2 * n / ms / 1e6}), flush=True)
 
 
-def decode_loop(torch, pp, dev, layers=32, steps=32, doc=12000, P=256, H=32, D=128, seed=1003, rope_base=1e6):
+def decode_loop(torch, pp, dev, layers=32, steps=32, doc=12000, P=256, H=32, D=128, seed=1003, rope_base=1e6,
+                with_oracle=True):
     """The answer loop of a 12000-token document with 256 streams: 32 steps of
     32 layers, each step appending one slot per stream (ids and plan once per
     step, then per layer: rotary embedding at the shared positions, append,
@@ -211,6 +228,18 @@ def decode_loop(torch, pp, dev, layers=32, steps=32, doc=12000, P=256, H=32, D=1
     torch.cuda.synchronize()
     timed(graph.replay)
     graph_ms = timed(graph.replay)
+    cpu = None
+    if with_oracle:
+        from oracle import oracle_append_step
+
+        b_last = base0 + (steps - 1) * P
+        kc, vc = K[0, :b_last + P].cpu(), V[0, :b_last + P].cpu()
+        qi, ki, vi = (x.cpu() for x in (qkv[0, 0], qkv[0, 1], qkv[0, 2]))
+        cpu = oracle_rate(lambda: oracle_append_step(qi, ki, vi, kc, vc, ids_full, b_last, scale, rope_base,
+                                                     streams=[0, 85, 170, 255]),
+                          4 / layers, "answer tok/s",
+                          f"one layer of the last step ({layers} per answer token) for 4 of {P} streams, all heads, "
+                          "including the append, rotation and fp64 conversion of that layer's cache")
     # KV bytes the loop reads: every layer-step reads the document and each
     # stream's own slots (its question and the answers so far, new one included)
     tail_slots = sum(sum(q_lens) + P * (t + 1) for t in range(steps))
@@ -226,10 +255,12 @@ def decode_loop(torch, pp, dev, layers=32, steps=32, doc=12000, P=256, H=32, D=1
         "effective_kv_gbs_graph": kv_bytes / (graph_ms / 1e3) / 1e9,
         "effective_kv_hbm_frac_graph": kv_bytes / (graph_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
         "inputs": "per-layer q/k/v reused across steps; caches N(0,1) bf16 from a seeded device generator",
+        "cpu_oracle": cpu,
     }
 
 
-def answer_sweep(torch, pp, dev, lengths=(128, 256, 512, 1024), doc=8192, P=128, H=32, D=128, seed=1005):
+def answer_sweep(torch, pp, dev, lengths=(128, 256, 512, 1024), doc=8192, P=128, H=32, D=128, seed=1005,
+                 with_oracle=True):
     """Long answers: an 8k-token document with 128 questions (16-32 tokens)
     and 128-1,024 answer tokens per stream already cached; one step through
     pp_attn_decode and through the per-question baseline."""
@@ -266,15 +297,23 @@ def answer_sweep(torch, pp, dev, lengths=(128, 256, 512, 1024), doc=8192, P=128,
         dm = t(pp.pp_attn_decode, 10, 2)
         bm = t(pp.pp_attn_decode_batched, 3, 1)
         kv = T * H * D * 2 * 2
-        rows.append({"answer_len": a, "seq_len": T, "decode_ms": dm, "batched_ms": bm, "speedup": bm / dm,
-                     "effective_kv_gbs": kv / (dm / 1e3) / 1e9})
+        row = {"answer_len": a, "seq_len": T, "decode_ms": dm, "batched_ms": bm, "speedup": bm / dm,
+               "effective_kv_gbs": kv / (dm / 1e3) / 1e9}
+        if with_oracle and a == lengths[-1]:
+            from oracle import oracle_decode
+
+            qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
+            row["cpu_oracle"] = oracle_rate(lambda: oracle_decode(qc, kc, vc, ids, T, 1.0 / math.sqrt(D),
+                                                                  streams=[0, P - 1]),
+                                            2, "answer tok/s", f"2 of {P} streams, all heads, one step")
+        rows.append(row)
         del q, k, v, sid, out, ws
         torch.cuda.empty_cache()
     return {"workload": f"codellama7b_doc8k_p{P}_answers{lengths[0]}-{lengths[-1]}", "P": P, "doc_len": doc,
             "questions": "uniform 16-32", "rows": rows}
 
 
-def prefill_bench(torch, pp, dev, doc=16384, P=256, H=32, D=128, seed=1006, runs=5):
+def prefill_bench(torch, pp, dev, doc=16384, P=256, H=32, D=128, seed=1006, runs=5, with_oracle=True):
     """Prefill of the packed request (the 16k-token document and 256
     questions of 8-48 tokens, one sequence): every slot attends causally
     under the stream rule."""
@@ -304,13 +343,23 @@ def prefill_bench(torch, pp, dev, doc=16384, P=256, H=32, D=128, seed=1006, runs
     # the whole document and its own question up to itself
     pairs = doc * (doc + 1) // 2 + sum(n * doc + n * (n + 1) // 2 for n in q_lens)
     flops = 4 * D * H * pairs
+    cpu = None
+    if with_oracle:
+        from oracle import oracle_prefill
+
+        qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
+        rows = [0, doc // 2, doc - 1, doc, (doc + T) // 2, T - 1, T - 2, T - 3]
+        cpu = oracle_rate(lambda: oracle_prefill(qc, kc, vc, ids, T, 1.0 / math.sqrt(D), rows=rows), len(rows),
+                          "prefilled tok/s", f"{len(rows)} of {T} slots (half of them question slots), all heads, "
+                          "including the fp64 conversion of q, k, v")
     return {"workload": f"codellama7b_prefill_doc16k_p{P}", "seq_len": T, "doc_len": doc, "P": P,
             "questions": "uniform 8-48", "ms": ms, "prefill_tok_s": T / (ms / 1e3),
             "visible_pairs_per_head": pairs, "tflops": flops / (ms / 1e3) / 1e12,
-            "mfma_frac": flops / (ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+            "mfma_frac": flops / (ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, "cpu_oracle": cpu}
 
 
-def multi_bench(torch, pp, dev, B=4, P=64, Hq=28, Hkv=4, D=128, doc=16384, a_len=31, seed=1007, steps=20):
+def multi_bench(torch, pp, dev, B=4, P=64, Hq=28, Hkv=4, D=128, doc=16384, a_len=31, seed=1007, steps=20,
+                with_oracle=True):
     """Several requests per launch with grouped key/value heads: 4 requests of
     64 streams (the pages' best streams per request is 16-64), each on its
     own 16k-token document, 28 query heads sharing 4 key/value heads (the
@@ -353,6 +402,14 @@ def multi_bench(torch, pp, dev, B=4, P=64, Hq=28, Hkv=4, D=128, doc=16384, a_len
 
     ms = t(False, steps)
     bms = t(True, max(3, steps // 4))
+    cpu = None
+    if with_oracle:
+        from oracle import oracle_decode
+
+        n0 = len(layouts[0])
+        qc, kc, vc = q[0].cpu(), k[0, :n0].cpu(), v[0, :n0].cpu()
+        cpu = oracle_rate(lambda: oracle_decode(qc, kc, vc, layouts[0], n0, 1.0 / math.sqrt(D), streams=[0, 21, 42, 63]),
+                          4, "answer tok/s", f"4 of the {P} streams of one request, all {Hq} query heads, one step")
     slot_bytes = Hkv * D * 2 * 2  # K + V of one slot, all key/value heads
     kv = (B * doc + q_total + B * P * a_len) * slot_bytes
     return {"workload": f"qwen2.5-7b-heads_{B}x{P}streams_doc16k", "B": B, "P": P, "Hq": Hq, "Hkv": Hkv, "d": D,
@@ -361,7 +418,7 @@ def multi_bench(torch, pp, dev, B=4, P=64, Hq=28, Hkv=4, D=128, doc=16384, a_len
             "effective_kv_hbm_frac": kv / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
             "tflops": 4 * D * Hq * B * P * doc / (ms / 1e3) / 1e12,
             "mfma_frac": 4 * D * Hq * B * P * doc / (ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-            "batched_baseline_ms": bms, "speedup_of_decode": bms / ms}
+            "batched_baseline_ms": bms, "speedup_of_decode": bms / ms, "cpu_oracle": cpu}
 
 
 def serving_bench(torch, pp, dev, R=16, B=4, P=16, Hq=28, Hkv=4, D=128, seed=1008):
@@ -582,24 +639,24 @@ def main():
     loop = None
     if not args.no_decode_loop:
         log("bench: 32-step x 32-layer appending loop")
-        loop = decode_loop(torch, pp, dev)
+        loop = decode_loop(torch, pp, dev, with_oracle=not args.no_cpu_baseline)
         torch.cuda.empty_cache()
 
     sweep = None
     if not args.no_answer_sweep:
         log("bench: long-answer sweep")
-        sweep = answer_sweep(torch, pp, dev)
+        sweep = answer_sweep(torch, pp, dev, with_oracle=not args.no_cpu_baseline)
 
     prefill = None
     if not args.no_prefill:
         log("bench: prefill")
-        prefill = prefill_bench(torch, pp, dev)
+        prefill = prefill_bench(torch, pp, dev, with_oracle=not args.no_cpu_baseline)
         torch.cuda.empty_cache()
 
     multi = None
     if not args.no_multi:
         log("bench: several requests, grouped heads")
-        multi = multi_bench(torch, pp, dev)
+        multi = multi_bench(torch, pp, dev, with_oracle=not args.no_cpu_baseline)
         torch.cuda.empty_cache()
 
     serving = None
