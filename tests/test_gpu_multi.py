@@ -89,3 +89,9 @@ def test_multi_full_size_sampled():
     out = _run(case)
     streams = [0, 17, 40, 63]
     _check(case, out, streams=streams, what="4 requests x 64 streams, 28/4 heads")
+
+
+def test_single_stream_single_head_requests():
+    case = multi_case(1, 1, 64, 1, [5, 0, 130, 1, 64], q_range=(1, 3), a_len=2, seed=31, name="p1h1")
+    _check(case, _run(case), what="P=1 H=1")
+    _check(case, _run(case, batched=True), what="P=1 H=1 baseline")

@@ -92,3 +92,12 @@ def test_prefill_full_size_sampled():
     say(f"  checking {len(rows)} rows of {T}")
     ref = _ref(case, rows=rows)
     assert_close(out[rows], ref[rows], what="prefill 16k document, 256 questions")
+
+
+@pytest.mark.parametrize("first_id", [0, 1])
+def test_prefill_single_slot(first_id):
+    case = prefill_case(2, 64, 1 if first_id == 0 else 0, [] if first_id == 0 else [1], seed=2, name="one slot")
+    assert case.seq_len == 1
+    out = _run(case)
+    # one visible key (itself): the output is its value
+    assert torch.equal(out.cpu(), case.v)

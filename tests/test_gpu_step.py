@@ -281,3 +281,16 @@ def test_full_size_appending_step_sampled():
     assert (diff <= _rot_bound(r["k_rot"], step_inp["k_new"].double().numpy())).all()
     assert (diff == 0).mean() > 0.99, (diff == 0).mean()
     assert r["pos"].tolist() == (doc + np.array([np.count_nonzero(ids_full[:b] == s + 1) for s in range(P)])).tolist()
+
+
+@pytest.mark.parametrize("P", [1, 300])
+def test_decode_append_stream_counts(P):
+    H, D = 2, 128
+    ids, T0, cap, k, v, q, kn, vn = _step_case(70 + P, P, H, D, doc=333, dtype=torch.bfloat16)
+    kg, vg, sid = k.to(DEV), v.to(DEV), _i32(ids)
+    say(f"  gpu: appending step P={P} T0={T0}")
+    plan = pp.pp_step_plan(sid, _i32([T0]), P, max_seq_len=cap)
+    out = pp.pp_attn_decode_append(q.to(DEV), kn.to(DEV), vn.to(DEV), kg, vg, sid, plan, rope_base=1e4)
+    torch.cuda.synchronize()
+    r = oracle_append_step(q, kn, vn, k, v, ids, T0, 1.0 / np.sqrt(D), 1e4)
+    assert_close(out, r["out"], what=f"appending step P={P}")
