@@ -11,6 +11,15 @@ q [P, H, d]; k_cache, v_cache [T >= seq_len, H, d] (bf16 or fp32, on the GPU,
 contiguous); stream_id [T] int32 with 0 = document, s+1 = stream s.  See
 the header for the exact definition and contract.
 
+The same kernels also serve: pp_attn_decode_batched (the per-question
+baseline), pp_attn_plan / pp_attn_decode_planned (one plan per step for all
+layers), pp_step_plan / pp_attn_decode_append (a step that appends one token
+per stream, rotary embedding at shared positions, graph-replayable),
+pp_attn_prefill (the packed request prefilled under the stream mask) and
+pp_attn_decode_multi (several requests per launch, grouped key/value heads,
+retired streams).  Schedules for refilling request slots are in
+``shared_prefix_stream_amd.batching``.
+
 If the library has not been built (``python -m shared_prefix_stream_amd.build``)
 every entry point raises; there is no fallback.
 """

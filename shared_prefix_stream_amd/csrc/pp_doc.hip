@@ -15,8 +15,12 @@
 // tail kernel merges them in a fixed order.
 //
 // Every document slot is visible to every stream, so no mask is evaluated
-// here beyond the split's slot range; slots outside it are zero-filled in
-// LDS, never loaded.
+// here beyond the split's slot range: rows of a ragged last tile re-read the
+// split's last row (finite data) and their scores are set to -inf.  Two
+// further modes share the kernel: grouped key/value heads (the G query heads
+// of a key/value head form one query tile, and several requests one grid)
+// and a causal mode for the prefill (query tile pt against the document
+// slots up to its own tile, masked above the diagonal).
 #include <math.h>
 
 #include <type_traits>
