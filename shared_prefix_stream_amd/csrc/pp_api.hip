@@ -417,7 +417,8 @@ pp_status_t pp_attn_prefill(const void* q, const void* k, const void* v, const i
   // the document length (a one-stream plan with no list), the causal
   // document part, then everything else per query slot
   hipError_t e = pp::launch_plan(stream_id, seq_len, 1, ws.plan, ws.counts, nullptr, 0, stream);
-  if (e == hipSuccess) e = pp::launch_doc(pl, q, k, v, seq_len, (int)seq_len, H, d, dtype, c, ws, stream, true);
+  if (e == hipSuccess)
+    e = pp::launch_doc(pl, q, k, v, seq_len, (int)seq_len, H, d, dtype, c, ws, stream, true, pp::Batch(), out);
   if (e == hipSuccess) e = pp::launch_prefill_rest(1, tile, q, k, v, stream_id, seq_len, H, d, dtype, c, ws, out, stream);
   if (e != hipSuccess) return fail(PP_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();

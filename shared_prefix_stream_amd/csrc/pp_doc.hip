@@ -149,12 +149,14 @@ __device__ __forceinline__ void wait_vmcnt() {
 // attends to the document slots j < min((pt + 1) * tile, doc_len) with
 // j <= i -- the part of every query's visible set that lies in the shared
 // document prefix up to its own tile.  One split per tile; tiles are taken
-// longest first.
+// longest first.  A document slot's whole visible set lies in its tile's
+// range, so with `out` given its output is final here and written directly
+// (the per-slot kernel that follows skips those slots).
 template <int D, int QB, int NW, bool CAUSAL>
 __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int P,
     int H, float c, const int32_t* __restrict__ plan, int64_t seq_len, int n_splits,
-    float* __restrict__ part_o, float2* __restrict__ part_ml, Batch bt) {
+    float* __restrict__ part_o, float2* __restrict__ part_ml, Batch bt, uint16_t* __restrict__ out) {
   using TL = DocTile<D, QB, NW>;
   constexpr int NK = TL::NK, NS = TL::NS, NLD = TL::NLD, ROWB = TL::ROWB, CPR = TL::CPR;
   constexpr int KC = D / 32;   // QK contraction steps (32 dims each)
@@ -191,7 +193,8 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
       qw[qb][kc] = *reinterpret_cast<const u32x4*>(q + qrow * D + kc * 32 + lg * 8);
   }
 
-  int L = (int)min<int64_t>(load_doc_len(plan + b), seq_len);  // a plan never exceeds the slots given
+  const int Ldoc = (int)min<int64_t>(load_doc_len(plan + b), seq_len);  // a plan never exceeds the slots given
+  int L = Ldoc;
   if constexpr (CAUSAL) L = min(L, (pt + 1) * (16 * QB * NW));
   // floor(i * n_tiles / n_splits) as i * (n / k) + i * (n % k) / k: 32-bit
   // arithmetic only (i <= n_splits <= 256)
@@ -587,7 +590,14 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
   for (int qb = 0; qb < QB; ++qb) {
     const float lt = lsum[qb][0];
     const int p = q0 + qb * 16 + ln;
-    if (p < PQ) {
+    if (CAUSAL && out && p < Ldoc) {  // (G = 1, B = 1 in the prefill: query p is slot p)
+      const float inv = 1.f / lt;  // a document slot sees at least slot 0
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        *reinterpret_cast<uint2*>(out + ((int64_t)p * Hq + h) * D + db * 16 + 4 * lg) =
+            make_uint2(pack_bf16x2(o[qb][db][0] * inv, o[qb][db][1] * inv),
+                       pack_bf16x2(o[qb][db][2] * inv, o[qb][db][3] * inv));
+    } else if (p < PQ) {
       const int64_t sh = ((int64_t)split * bt.B * P + b * P + p / G) * Hq + h * G + p % G;
       // reference of the split's state: 0 in the fast pass, the running
       // maximum in the exact pass; an empty split has none (-inf)
@@ -610,7 +620,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kDocThreads) void doc_valu_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v, int P, int H, float c,
     const int32_t* __restrict__ plan, int64_t seq_len, int n_splits, float* __restrict__ part_o,
-    float2* __restrict__ part_ml, Batch bt) {
+    float2* __restrict__ part_ml, Batch bt, float* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) float lk[kF32NK][D];
   __shared__ __attribute__((aligned(16))) float lv[kF32NK][D];
   const int split = blockIdx.x, h = blockIdx.y;
@@ -622,7 +632,8 @@ __global__ __launch_bounds__(kDocThreads) void doc_valu_f32_kernel(
   const int G = bt.G, PQ = P * G, Hq = H * G;
   k += b * bt.kv_stride;
   v += b * bt.kv_stride;
-  int L = (int)min<int64_t>(load_doc_len(plan + b), seq_len);  // a plan never exceeds the slots given
+  const int Ldoc = (int)min<int64_t>(load_doc_len(plan + b), seq_len);  // a plan never exceeds the slots given
+  int L = Ldoc;
   if constexpr (CAUSAL) L = min(L, (pt + 1) * kDocThreads);  // see doc_mfma_bf16_kernel
   const int n_tiles = (L + kF32NK - 1) / kF32NK;
   const int t0 = (int)((int64_t)split * n_tiles / n_splits);
@@ -677,7 +688,13 @@ __global__ __launch_bounds__(kDocThreads) void doc_valu_f32_kernel(
     }
     __syncthreads();
   }
-  if (p < PQ) {
+  if (CAUSAL && out && p < Ldoc) {  // a document slot's output is final (see doc_mfma_bf16_kernel)
+    const float inv = 1.f / l;
+#pragma unroll
+    for (int e = 0; e < D; e += 4)
+      *reinterpret_cast<float4*>(out + ((int64_t)p * Hq + h) * D + e) =
+          make_float4(acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv);
+  } else if (p < PQ) {
     const int64_t sh = ((int64_t)split * bt.B * P + b * P + p / G) * Hq + h * G + p % G;
     part_ml[sh] = make_float2(m, l);
 #pragma unroll
@@ -722,7 +739,7 @@ int doc_query_tile(const DocPlan& pl, pp_dtype_t dtype) {
 
 hipError_t launch_doc(const DocPlan& pl, const void* q, const void* k, const void* v, int64_t seq_len, int P, int H,
                       int d, pp_dtype_t dtype, float c, const Workspace& ws, hipStream_t stream, bool causal,
-                      const Batch& bt) {
+                      const Batch& bt, void* out) {
   const dim3 grid(pl.n_splits, H, pl.n_ptiles * bt.B);
   if (dtype == PP_BF16) {
     auto* qq = static_cast<const uint16_t*>(q);
@@ -730,9 +747,10 @@ hipError_t launch_doc(const DocPlan& pl, const void* q, const void* k, const voi
     auto* vv = static_cast<const uint16_t*>(v);
 #define PP_DOC_LAUNCH(DD, QQ, WW)                                                                           \
   (causal ? doc_mfma_bf16_kernel<DD, QQ, WW, true><<<grid, 64 * WW, 0, stream>>>(                                 \
-                qq, kk, vv, P, H, c, ws.plan, seq_len, pl.n_splits, ws.part_o, ws.part_ml, bt)                    \
+                qq, kk, vv, P, H, c, ws.plan, seq_len, pl.n_splits, ws.part_o, ws.part_ml, bt,                   \
+                static_cast<uint16_t*>(out))                                                                 \
           : doc_mfma_bf16_kernel<DD, QQ, WW, false><<<grid, 64 * WW, 0, stream>>>(                                \
-                qq, kk, vv, P, H, c, ws.plan, seq_len, pl.n_splits, ws.part_o, ws.part_ml, bt))
+                qq, kk, vv, P, H, c, ws.plan, seq_len, pl.n_splits, ws.part_o, ws.part_ml, bt, nullptr))
     // dispatch on the exact (d, 16-query blocks per wave, waves) triple
     const int cfg = d * 10000 + pl.qb * 100 + pl.nw;
     switch (cfg) {
@@ -750,7 +768,7 @@ hipError_t launch_doc(const DocPlan& pl, const void* q, const void* k, const voi
     auto* kk = static_cast<const float*>(k);
     auto* vv = static_cast<const float*>(v);
 #define PP_F32_LAUNCH(DD, CC) \
-  doc_valu_f32_kernel<DD, CC><<<grid, kDocThreads, 0, stream>>>(qq, kk, vv, P, H, c, ws.plan, seq_len, pl.n_splits, ws.part_o, ws.part_ml, bt)
+  doc_valu_f32_kernel<DD, CC><<<grid, kDocThreads, 0, stream>>>(qq, kk, vv, P, H, c, ws.plan, seq_len, pl.n_splits, ws.part_o, ws.part_ml, bt, static_cast<float*>(out))
     if (d == 128) {
       if (causal) PP_F32_LAUNCH(128, true);
       else PP_F32_LAUNCH(128, false);

@@ -322,11 +322,12 @@ DocPlan choose_doc_plan(int64_t seq_len, int P, int H, int d, pp_dtype_t dtype, 
 // Queries per workgroup of the document kernel for this plan (its query tile).
 int doc_query_tile(const DocPlan& plan, pp_dtype_t dtype);
 // causal: prefill -- query i is slot i and query tile pt sees the document
-// slots j < min((pt + 1) * tile, doc_len) with j <= i (one split).
+// slots j < min((pt + 1) * tile, doc_len) with j <= i (one split); with out
+// given, the rows of document slots (complete there) are written to it.
 // (P: streams per request, H: key/value heads; the grid covers bt.B requests)
 hipError_t launch_doc(const DocPlan& plan, const void* q, const void* k, const void* v, int64_t seq_len, int P,
                       int H, int d, pp_dtype_t dtype, float scale_log2, const Workspace& ws, hipStream_t stream,
-                      bool causal = false, const Batch& bt = Batch());
+                      bool causal = false, const Batch& bt = Batch(), void* out = nullptr);
 
 // Per-question document part (the "batched requests" baseline): every
 // stream reads the document itself.
@@ -344,11 +345,11 @@ hipError_t launch_tail_merge(int n_splits, const void* q, const void* k, const v
                              float scale_log2, const Workspace& ws, void* out, hipStream_t stream,
                              const Batch& bt = Batch());
 
-// Prefill: for every query slot i < seq_len, the visible slots the
-// document kernel (causal, query tile `tile`) left out -- j in
+// Prefill: for every query slot i in [doc_len, seq_len), the visible slots
+// the document kernel (causal, query tile `tile`) left out -- j in
 // [min((i / tile + 1) * tile, doc_len), i] with id 0 or id[i] -- compacted
 // from stream_id, gathered, merged with the document partial of row i, and
-// out[i] written.
+// out[i] written (document slots were written by the document kernel).
 hipError_t launch_prefill_rest(int n_splits, int tile, const void* q, const void* k, const void* v,
                                const int32_t* sid, int64_t seq_len, int H, int d, pp_dtype_t dtype, float scale_log2,
                                const Workspace& ws, void* out, hipStream_t stream);

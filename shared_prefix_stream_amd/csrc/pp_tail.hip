@@ -87,7 +87,8 @@ __device__ __forceinline__ void merge_state(float& M, float& Ls, float* A, float
 // PREFILL: blockIdx.x is a query slot i (q, out and the partials have one
 // row per slot), and its list is compacted here from stream_id: the slots
 // j in [min((i / tile + 1) * tile, doc_len), i] with id 0 or id[i] -- what
-// the causal document kernel did not cover of i's visible set.
+// the causal document kernel did not cover of i's visible set.  Slots below
+// doc_len are complete in the document kernel, which wrote them.
 template <typename T, int D, bool PREFILL>
 // (at most 128 VGPRs: four workgroups per CU)
 __global__ __launch_bounds__(kTailThreads, 4) void tail_merge_kernel(
@@ -117,6 +118,7 @@ __global__ __launch_bounds__(kTailThreads, 4) void tail_merge_kernel(
   // (the substream index is wave-uniform; readfirstlane lets the compiler know)
   const int tid = threadIdx.x, ts = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int64_t row = (int64_t)(H / bt.G) * D;  // key/value heads
+  if (PREFILL && s < load_doc_len(plan)) return;  // a document slot: written by the document kernel
   if (!PREFILL && !stream_active(bt, s)) {  // a retired stream: zeros, no work (workgroup-uniform)
     const int head0 = hg * S::GW;
     const int nel = (min(H, head0 + S::GW) - head0) * D;
