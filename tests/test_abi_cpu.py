@@ -251,3 +251,38 @@ def test_python_binding_rejects_cpu_tensors():
     q = torch.zeros(2, 1, 64)
     with pytest.raises(ValueError):
         pp.pp_attn_decode(q, q, q, torch.zeros(2, dtype=torch.int32))
+
+
+def test_python_bindings_of_the_extensions_reject_host_tensors():
+    # every binding checks its tensors before calling the library: host
+    # tensors (there is no GPU here) are refused with ValueError
+    import torch
+
+    q = torch.zeros(2, 1, 64, dtype=torch.bfloat16)
+    sid = torch.zeros(8, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        pp.pp_attn_decode_batched(q, q, q, sid)
+    with pytest.raises(ValueError):
+        pp.pp_attn_decode_planned(q, q, q, sid, (sid[:1], sid[:2], sid[:2].view(2, 1)))
+    with pytest.raises(ValueError):
+        pp.pp_attn_plan(sid, 8, 2)
+    with pytest.raises(ValueError):
+        pp.pp_step_plan(sid, torch.zeros(1, dtype=torch.int32), 2)
+    with pytest.raises(ValueError):
+        pp.pp_attn_decode_append(q, q, q, q, q, sid, (sid[:2], sid[:2], sid[:2].view(2, 1)))
+    with pytest.raises(ValueError):
+        pp.pp_attn_prefill(q, q, q, sid[:2])
+    q4 = torch.zeros(1, 2, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        pp.pp_attn_decode_multi(q4, q4, q4, sid.view(1, 8), torch.ones(1, dtype=torch.int32))
+
+
+def test_bench_refuses_several_gpus():
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(__file__))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       cwd=root, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in r.stderr
