@@ -113,6 +113,29 @@ def test_foreign_ids_see_the_document_and_their_own_id():
     assert prefill_visible(ids, 6).tolist() == [0, 1, 3, 5, 6]
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(6, 2), (7, 1)])
+def test_grouped_heads_document_only_is_grouped_causal_sdpa(Hq, Hkv):
+    rng = np.random.default_rng(Hq)
+    T = 19
+    q = rng.standard_normal((T, Hq, 8))
+    k = rng.standard_normal((T, Hkv, 8))
+    v = rng.standard_normal((T, Hkv, 8))
+    got = oracle_prefill(q, k, v, np.zeros(T, dtype=np.int32), T, 0.6)
+    t = [torch.from_numpy(x).permute(1, 0, 2).unsqueeze(0) for x in (q, k, v)]
+    ref = torch.nn.functional.scaled_dot_product_attention(*t, is_causal=True, scale=0.6, enable_gqa=True)
+    np.testing.assert_allclose(got, ref.squeeze(0).permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_grouped_heads_equal_repeated_heads_in_prefill():
+    rng = np.random.default_rng(3)
+    ids, _ = canonical_layout(6, [3, 2], [1, 2])
+    T = len(ids)
+    q, k, v = rng.standard_normal((T, 4, 8)), rng.standard_normal((T, 2, 8)), rng.standard_normal((T, 2, 8))
+    a = oracle_prefill(q, k, v, ids, T, 0.5)
+    b = oracle_prefill(q, np.repeat(k, 2, axis=1), np.repeat(v, 2, axis=1), ids, T, 0.5)
+    np.testing.assert_array_equal(a, b)
+
+
 # ---------------------------------------------------------------- mutants ---
 
 MUTANTS = {
@@ -120,6 +143,8 @@ MUTANTS = {
     "document dropped": ("(ids == 0) | (ids == ids[i])", "(ids == ids[i])"),
     "other streams seen": ("(ids == 0) | (ids == ids[i])", "(ids == 0) | (ids >= 0)"),
     "not causal": ("ids = np.asarray(stream_id)[: i + 1]", "ids = np.asarray(stream_id)"),
+    "grouped heads read the wrong key head": ("attend(qf[i, h], kf[h // G], vf[h // G], idx, scale)",
+                                              "attend(qf[i, h], kf[h % kf.shape[0]], vf[h % kf.shape[0]], idx, scale)"),
 }
 
 
@@ -149,9 +174,14 @@ def _pins_pass(mod) -> bool:
     w /= w.sum(-1, keepdims=True)
     try:
         got = mod.oracle_prefill(q, k, v, ids, T, 1.0)
+        qg, kg = rng.standard_normal((7, 4, 8)), rng.standard_normal((7, 2, 8))
+        gqa = mod.oracle_prefill(qg, kg, kg, np.zeros(7, dtype=np.int32), 7, 0.5)
     except Exception:
         return False
-    return bool(np.allclose(got, np.einsum("hij,jhd->ihd", w, v), rtol=0, atol=1e-12))
+    t = [torch.from_numpy(x).permute(1, 0, 2).unsqueeze(0) for x in (qg, kg, kg)]
+    ref = torch.nn.functional.scaled_dot_product_attention(*t, is_causal=True, scale=0.5, enable_gqa=True)
+    ok_gqa = np.allclose(gqa, ref.squeeze(0).permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+    return bool(np.allclose(got, np.einsum("hij,jhd->ihd", w, v), rtol=0, atol=1e-12)) and bool(ok_gqa)
 
 
 def test_unmutated_copy_passes():
