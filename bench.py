@@ -313,7 +313,7 @@ def answer_sweep(torch, pp, dev, lengths=(128, 256, 512, 1024), doc=8192, P=128,
             "questions": "uniform 16-32", "rows": rows}
 
 
-def prefill_bench(torch, pp, dev, doc=16384, P=256, H=32, D=128, seed=1006, runs=5, with_oracle=True):
+def prefill_bench(torch, pp, dev, doc=16384, P=256, H=32, D=128, seed=1006, runs=5, with_oracle=True, Hkv=None):
     """Prefill of the packed request (the 16k-token document and 256
     questions of 8-48 tokens, one sequence): every slot attends causally
     under the stream rule."""
@@ -326,7 +326,9 @@ def prefill_bench(torch, pp, dev, doc=16384, P=256, H=32, D=128, seed=1006, runs
     ids, _ = canonical_layout(doc, q_lens, [0] * P)
     T = len(ids)
     g = torch.Generator(device=dev).manual_seed(seed)
-    q, k, v = (torch.randn(T, H, D, generator=g, device=dev, dtype=torch.bfloat16) for _ in range(3))
+    hk = H if Hkv is None else Hkv
+    q = torch.randn(T, H, D, generator=g, device=dev, dtype=torch.bfloat16)
+    k, v = (torch.randn(T, hk, D, generator=g, device=dev, dtype=torch.bfloat16) for _ in range(2))
     sid = torch.from_numpy(ids).to(dev)
     out = torch.empty_like(q)
     ws = torch.empty(pp.prefill_workspace_bytes(T, H, D, torch.bfloat16), dtype=torch.uint8, device=dev)
@@ -352,7 +354,8 @@ def prefill_bench(torch, pp, dev, doc=16384, P=256, H=32, D=128, seed=1006, runs
         cpu = oracle_rate(lambda: oracle_prefill(qc, kc, vc, ids, T, 1.0 / math.sqrt(D), rows=rows), len(rows),
                           "prefilled tok/s", f"{len(rows)} of {T} slots (half of them question slots), all heads, "
                           "including the fp64 conversion of q, k, v")
-    return {"workload": f"codellama7b_prefill_doc16k_p{P}", "seq_len": T, "doc_len": doc, "P": P,
+    name = f"codellama7b_prefill_doc16k_p{P}" if Hkv is None else f"qwen2.5-7b-heads_prefill_doc16k_p{P}"
+    return {"workload": name, "seq_len": T, "doc_len": doc, "P": P, "Hq": H, "Hkv": hk,
             "questions": "uniform 8-48", "ms": ms, "prefill_tok_s": T / (ms / 1e3),
             "visible_pairs_per_head": pairs, "tflops": flops / (ms / 1e3) / 1e12,
             "mfma_frac": flops / (ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, "cpu_oracle": cpu}
@@ -651,6 +654,7 @@ def main():
     if not args.no_prefill:
         log("bench: prefill")
         prefill = prefill_bench(torch, pp, dev, with_oracle=not args.no_cpu_baseline)
+        prefill["grouped_heads"] = prefill_bench(torch, pp, dev, H=28, Hkv=4, with_oracle=False)
         torch.cuda.empty_cache()
 
     multi = None

@@ -259,16 +259,18 @@ pp_status_t pp_attn_decode_append(const void* q, const void* k_new, const void* 
  *   out[i,h,:] = sum_{j in V(i)} softmax_j(scale * dot(q[i,h,:], k[j,h,:])) * v[j,h,:]
  * A document slot sees the document up to itself; a stream's slot sees the
  * whole document before it and its own stream's slots up to itself (never
- * another stream's).  Layouts: q, k, v, out [seq_len, H, d] of `dtype`,
- * stream_id [seq_len] int32, contiguous, 16-byte aligned, device memory;
+ * another stream's).  Layouts: q, out [seq_len, Hq, d] and k, v
+ * [seq_len, Hkv, d] of `dtype` (Hq a multiple of Hkv: query head h reads
+ * key/value head h / (Hq / Hkv); Hkv = Hq without grouping), stream_id
+ * [seq_len] int32, contiguous, 16-byte aligned, device memory;
  * seq_len <= 65535 * 256.  The leading run of id-0 slots is contracted on
  * the matrix cores in query tiles (causal inside the run); each slot's
  * remaining visible slots past that run are compacted from stream_id and
  * gathered.  Workspace: pp_attn_prefill_workspace_bytes(seq_len, H, d,
  * dtype) bytes.  Contract, asynchrony and errors as pp_attn_decode. */
-size_t pp_attn_prefill_workspace_bytes(int64_t seq_len, int32_t H, int32_t d, pp_dtype_t dtype);
+size_t pp_attn_prefill_workspace_bytes(int64_t seq_len, int32_t Hq, int32_t d, pp_dtype_t dtype);
 pp_status_t pp_attn_prefill(const void* q, const void* k, const void* v, const int32_t* stream_id,
-                            int64_t seq_len, int32_t H, int32_t d, float scale, void* out,
+                            int64_t seq_len, int32_t Hq, int32_t Hkv, int32_t d, float scale, void* out,
                             pp_dtype_t dtype, void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* Profiling variant of pp_attn_decode (batched == 0) or pp_attn_decode_batched

@@ -116,7 +116,7 @@ def _load():
     lib.pp_attn_prefill_workspace_bytes.restype = sz
     lib.pp_attn_prefill_workspace_bytes.argtypes = [i64, i32, i32, ctypes.c_int]
     lib.pp_attn_prefill.restype = ctypes.c_int
-    lib.pp_attn_prefill.argtypes = [vp, vp, vp, vp, i64, i32, i32, f32, vp, ctypes.c_int, vp, sz, vp]
+    lib.pp_attn_prefill.argtypes = [vp, vp, vp, vp, i64, i32, i32, i32, f32, vp, ctypes.c_int, vp, sz, vp]
     lib.pp_attn_multi_workspace_bytes.restype = sz
     lib.pp_attn_multi_workspace_bytes.argtypes = [i64, i32, i32, i32, i32, i32, ctypes.c_int]
     for name in ("pp_attn_decode_multi", "pp_attn_decode_multi_batched"):
@@ -385,16 +385,16 @@ def prefill_workspace_bytes(seq_len: int, H: int, d: int, dtype) -> int:
 def pp_attn_prefill(q, k, v, stream_id, seq_len: Optional[int] = None, scale: Optional[float] = None, out=None,
                     workspace=None):
     """Prefill of the packed request: every slot i < seq_len attends to the
-    slots j <= i holding the document (id 0) or its own id.  q, k, v
-    [T >= seq_len, H, d] on the GPU; returns out [T, H, d] (rows >= seq_len
-    untouched) without synchronising."""
+    slots j <= i holding the document (id 0) or its own id.  q [T >= seq_len,
+    Hq, d], k, v [T, Hkv, d] (Hq a multiple of Hkv) on the GPU; returns out
+    [T, Hq, d] (rows >= seq_len untouched) without synchronising."""
     import torch
 
     for name, t in (("q", q), ("k", k), ("v", v), ("stream_id", stream_id)):
         if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous GPU tensor")
-    if q.dim() != 3 or q.shape != k.shape or q.shape != v.shape:
-        raise ValueError("q, k and v must share one [T, H, d] shape")
+    if q.dim() != 3 or k.dim() != 3 or k.shape != v.shape or k.shape[0] != q.shape[0] or k.shape[2] != q.shape[2]:
+        raise ValueError("q must be [T, Hq, d] and k, v [T, Hkv, d]")
     if not (q.dtype == k.dtype == v.dtype):
         raise ValueError("q, k and v must share one dtype")
     if stream_id.dtype != torch.int32 or stream_id.dim() != 1:
@@ -411,8 +411,8 @@ def pp_attn_prefill(q, k, v, stream_id, seq_len: Optional[int] = None, scale: Op
         raise ValueError("out must be a contiguous GPU tensor shaped and typed like q")
     if workspace is None:
         workspace = torch.empty(prefill_workspace_bytes(seq_len, H, d, code), dtype=torch.uint8, device=q.device)
-    _check(_load().pp_attn_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), stream_id.data_ptr(), seq_len, H, d,
-                                   scale, out.data_ptr(), code, workspace.data_ptr(),
+    _check(_load().pp_attn_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), stream_id.data_ptr(), seq_len, H,
+                                   int(k.shape[1]), d, scale, out.data_ptr(), code, workspace.data_ptr(),
                                    workspace.numel() * workspace.element_size(), _stream_handle(q.device)))
     return out
 

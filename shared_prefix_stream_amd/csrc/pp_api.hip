@@ -387,39 +387,48 @@ size_t pp_attn_prefill_workspace_bytes(int64_t seq_len, int32_t H, int32_t d, pp
 }
 
 pp_status_t pp_attn_prefill(const void* q, const void* k, const void* v, const int32_t* stream_id, int64_t seq_len,
-                            int32_t H, int32_t d, float scale, void* out, pp_dtype_t dtype, void* workspace,
-                            size_t workspace_bytes, void* hip_stream) {
-  pp_status_t st = check_prefill_shape(seq_len, H, d, dtype);
+                            int32_t Hq, int32_t Hkv, int32_t d, float scale, void* out, pp_dtype_t dtype,
+                            void* workspace, size_t workspace_bytes, void* hip_stream) {
+  pp_status_t st = check_prefill_shape(seq_len, Hq, d, dtype);
   if (st != PP_OK) return st;
+  if (Hkv < 1 || Hq % Hkv != 0) return fail(PP_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
   if (!q || !k || !v || !stream_id || !out) return fail(PP_ERR_INVALID_ARG, "null q, k, v, stream_id or out");
   if (!isfinite(scale)) return fail(PP_ERR_INVALID_ARG, "scale is not finite");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(stream_id) || !aligned16(out))
     return fail(PP_ERR_INVALID_ARG, "q, k, v, stream_id and out must be 16-byte aligned");
-  const size_t n = (size_t)seq_len * H * d * elem_size(dtype), nid = (size_t)seq_len * 4;
-  if (overlaps(out, n, q, n) || overlaps(out, n, k, n) || overlaps(out, n, v, n) || overlaps(out, n, stream_id, nid) ||
-      overlaps(out, n, workspace, workspace_bytes))
+  const size_t n = (size_t)seq_len * Hq * d * elem_size(dtype), nkv = (size_t)seq_len * Hkv * d * elem_size(dtype),
+               nid = (size_t)seq_len * 4;
+  if (overlaps(out, n, q, n) || overlaps(out, n, k, nkv) || overlaps(out, n, v, nkv) ||
+      overlaps(out, n, stream_id, nid) || overlaps(out, n, workspace, workspace_bytes))
     return fail(PP_ERR_INVALID_ARG, "out overlaps an input or the workspace");
-  if (overlaps(workspace, workspace_bytes, q, n) || overlaps(workspace, workspace_bytes, k, n) ||
-      overlaps(workspace, workspace_bytes, v, n) || overlaps(workspace, workspace_bytes, stream_id, nid))
+  if (overlaps(workspace, workspace_bytes, q, n) || overlaps(workspace, workspace_bytes, k, nkv) ||
+      overlaps(workspace, workspace_bytes, v, nkv) || overlaps(workspace, workspace_bytes, stream_id, nid))
     return fail(PP_ERR_INVALID_ARG, "workspace overlaps an input");
-  const size_t need = prefill_bytes(seq_len, H, d);
+  const size_t need = prefill_bytes(seq_len, Hq, d);
   if (!workspace || workspace_bytes < need)
     return fail(PP_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : (size_t)0, need);
   int cus = 0;
   if (!num_cus(&cus)) return fail(PP_ERR_HIP, "could not query the current device's compute-unit count");
   if (cus > kSizingCus) cus = kSizingCus;
-  pp::DocPlan pl = pp::choose_doc_plan(seq_len, (int)seq_len, H, d, dtype, cus);
+  pp::DocPlan pl = pp::choose_doc_plan(seq_len, (int)seq_len, Hq, d, dtype, cus);
   pl.n_splits = 1;  // the causal document kernel covers each query tile's prefix in one workgroup
   const int tile = pp::doc_query_tile(pl, dtype);
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   const float c = (float)((double)scale * 1.4426950408889634074);
-  const pp::Workspace ws = carve_prefill(workspace, seq_len, H);
+  const pp::Workspace ws = carve_prefill(workspace, seq_len, Hq);
+  // grouped key/value heads: the causal document kernel runs one workgroup
+  // row per query head (query tiles stay aligned with slots), each reading
+  // its group's key/value head; the per-slot kernel maps heads the same way
+  pp::Batch doc_bt, rest_bt;
+  doc_bt.kv_group = Hq / Hkv;
+  rest_bt.G = Hq / Hkv;
   // the document length (a one-stream plan with no list), the causal
   // document part, then everything else per query slot
   hipError_t e = pp::launch_plan(stream_id, seq_len, 1, ws.plan, ws.counts, nullptr, 0, stream);
   if (e == hipSuccess)
-    e = pp::launch_doc(pl, q, k, v, seq_len, (int)seq_len, H, d, dtype, c, ws, stream, true, pp::Batch(), out);
-  if (e == hipSuccess) e = pp::launch_prefill_rest(1, tile, q, k, v, stream_id, seq_len, H, d, dtype, c, ws, out, stream);
+    e = pp::launch_doc(pl, q, k, v, seq_len, (int)seq_len, Hq, d, dtype, c, ws, stream, true, doc_bt, out);
+  if (e == hipSuccess)
+    e = pp::launch_prefill_rest(1, tile, q, k, v, stream_id, seq_len, Hq, d, dtype, c, ws, out, stream, rest_bt);
   if (e != hipSuccess) return fail(PP_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }

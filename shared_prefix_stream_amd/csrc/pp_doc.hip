@@ -174,7 +174,10 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int ln = lane & 15, lg = lane >> 4;
   const int q0 = pt * (16 * QB * NW) + wave * (16 * QB);
-  const int64_t row = (int64_t)H * D;  // elements between consecutive slots (key/value heads)
+  // elements between consecutive slots (key/value heads), and this
+  // workgroup's key/value head (grid.y runs over query heads when unfolded)
+  const int64_t row = (int64_t)(H / bt.kv_group) * D;
+  const int hk = h / bt.kv_group;
   const int G = bt.G, PQ = P * G, Hq = H * G;
   k += b * bt.kv_stride;
   v += b * bt.kv_stride;
@@ -266,8 +269,8 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
       const int blk = i * NW + wave_u + 4 * sset;
       const int r = blk * TL::ROWS_PER_KB + lane / CPR;
       const int slot = lane % CPR;
-      koff[sset][i] = (uint32_t)(((int64_t)r * row + (int64_t)h * D + (slot ^ swz_k<D>(r)) * 8) * 2);
-      voff[sset][i] = (uint32_t)(((int64_t)r * row + (int64_t)h * D + (slot ^ swz_v<D>(r)) * 8) * 2);
+      koff[sset][i] = (uint32_t)(((int64_t)r * row + (int64_t)hk * D + (slot ^ swz_k<D>(r)) * 8) * 2);
+      voff[sset][i] = (uint32_t)(((int64_t)r * row + (int64_t)hk * D + (slot ^ swz_v<D>(r)) * 8) * 2);
     }
   auto issue = [&](int t) __attribute__((always_inline)) {
     // (wave-uniform; stated so the value stays on the scalar unit for m0)
@@ -295,7 +298,7 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
           const int blk = i * NW + wave_u + 4 * sset;
           const int r = blk * TL::ROWS_PER_KB + lane / CPR;
           const int slot = lane % CPR;
-          const int64_t g = (int64_t)min(kbase + r, key_end - 1) * row + (int64_t)h * D;
+          const int64_t g = (int64_t)min(kbase + r, key_end - 1) * row + (int64_t)hk * D;
           lds_dma16(k + g + (slot ^ swz_k<D>(r)) * 8, ks + blk * 1024);
           lds_dma16(v + g + (slot ^ swz_v<D>(r)) * 8, vs + blk * 1024);
         }
@@ -639,7 +642,7 @@ __global__ __launch_bounds__(kDocThreads) void doc_valu_f32_kernel(
   const int t0 = (int)((int64_t)split * n_tiles / n_splits);
   const int t1 = (int)((int64_t)(split + 1) * n_tiles / n_splits);
   const int key_end = min(t1 * kF32NK, L);
-  const int64_t row = (int64_t)H * D;
+  const int64_t row = (int64_t)(H / bt.kv_group) * D;  // key/value heads (see doc_mfma_bf16_kernel)
 
   float qv[D], acc[D];
 #pragma unroll
@@ -656,8 +659,8 @@ __global__ __launch_bounds__(kDocThreads) void doc_valu_f32_kernel(
       const int gk = kbase + key;
       float4 kk = make_float4(0.f, 0.f, 0.f, 0.f), vv = kk;
       if (gk < key_end) {
-        kk = *reinterpret_cast<const float4*>(k + (int64_t)gk * row + (int64_t)h * D + col * 4);
-        vv = *reinterpret_cast<const float4*>(v + (int64_t)gk * row + (int64_t)h * D + col * 4);
+        kk = *reinterpret_cast<const float4*>(k + (int64_t)gk * row + (int64_t)(h / bt.kv_group) * D + col * 4);
+        vv = *reinterpret_cast<const float4*>(v + (int64_t)gk * row + (int64_t)(h / bt.kv_group) * D + col * 4);
       }
       *reinterpret_cast<float4*>(&lk[key][col * 4]) = kk;
       *reinterpret_cast<float4*>(&lv[key][col * 4]) = vv;

@@ -37,6 +37,9 @@ struct Batch {
   int64_t id_stride = 0;               // ids between requests' stream_id arrays
   const int32_t* seq_lens = nullptr;   // per-request lengths on the device (else seq_len for all)
   const int32_t* active = nullptr;     // per launch stream: 0 = retired (sees nothing, output 0); null: all
+  // document kernel without folding (the causal prefill): grid.y runs over
+  // query heads and head h reads key/value head h / kv_group
+  int kv_group = 1;
 };
 
 __device__ __forceinline__ bool stream_active(const Batch& bt, int s) {
@@ -352,6 +355,6 @@ hipError_t launch_tail_merge(int n_splits, const void* q, const void* k, const v
 // out[i] written (document slots were written by the document kernel).
 hipError_t launch_prefill_rest(int n_splits, int tile, const void* q, const void* k, const void* v,
                                const int32_t* sid, int64_t seq_len, int H, int d, pp_dtype_t dtype, float scale_log2,
-                               const Workspace& ws, void* out, hipStream_t stream);
+                               const Workspace& ws, void* out, hipStream_t stream, const Batch& bt = Batch());
 
 }  // namespace pp

@@ -318,13 +318,14 @@ hipError_t launch_tail_merge(int n_splits, const void* q, const void* k, const v
 
 hipError_t launch_prefill_rest(int n_splits, int tile, const void* q, const void* k, const void* v,
                                const int32_t* sid, int64_t seq_len, int H, int d, pp_dtype_t dtype, float c,
-                               const Workspace& ws, void* out, hipStream_t stream) {
+                               const Workspace& ws, void* out, hipStream_t stream, const Batch& bt) {
   const int P = (int)seq_len;  // one query per slot
   if (dtype == PP_BF16)
-    return d == 128 ? launch_tail_t<uint16_t, 128, true>(n_splits, q, k, v, sid, seq_len, P, H, c, ws, out, stream, tile)
-                    : launch_tail_t<uint16_t, 64, true>(n_splits, q, k, v, sid, seq_len, P, H, c, ws, out, stream, tile);
-  return d == 128 ? launch_tail_t<float, 128, true>(n_splits, q, k, v, sid, seq_len, P, H, c, ws, out, stream, tile)
-                  : launch_tail_t<float, 64, true>(n_splits, q, k, v, sid, seq_len, P, H, c, ws, out, stream, tile);
+    return d == 128
+               ? launch_tail_t<uint16_t, 128, true>(n_splits, q, k, v, sid, seq_len, P, H, c, ws, out, stream, tile, bt)
+               : launch_tail_t<uint16_t, 64, true>(n_splits, q, k, v, sid, seq_len, P, H, c, ws, out, stream, tile, bt);
+  return d == 128 ? launch_tail_t<float, 128, true>(n_splits, q, k, v, sid, seq_len, P, H, c, ws, out, stream, tile, bt)
+                  : launch_tail_t<float, 64, true>(n_splits, q, k, v, sid, seq_len, P, H, c, ws, out, stream, tile, bt);
 }
 
 }  // namespace pp

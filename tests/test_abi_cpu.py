@@ -204,13 +204,15 @@ def test_prefill_validation():
     n = lib.pp_attn_prefill_workspace_bytes(1000, 4, 128, pp.PP_BF16)
     assert n >= 1000 * 4 * (128 + 2) * 4  # one fp32 partial state per (slot, head)
 
-    def call(q=Q, k=K, v=V, sid=SID, T=1000, out=OUT, ws=WS, wsb=n, scale=0.088, d=128):
-        return lib.pp_attn_prefill(q, k, v, sid, T, 4, d, scale, out, pp.PP_BF16, ws, wsb, None)
+    def call(q=Q, k=K, v=V, sid=SID, T=1000, out=OUT, ws=WS, wsb=n, scale=0.088, d=128, hkv=4):
+        return lib.pp_attn_prefill(q, k, v, sid, T, 4, hkv, d, scale, out, pp.PP_BF16, ws, wsb, None)
 
     assert call(q=None) == pp.PP_ERR_INVALID_ARG
     assert call(sid=None) == pp.PP_ERR_INVALID_ARG
     assert call(T=0) == pp.PP_ERR_INVALID_ARG
     assert call(d=96) == pp.PP_ERR_UNSUPPORTED
+    assert call(hkv=3) == pp.PP_ERR_INVALID_ARG               # 4 query heads cannot share 3
+    assert call(hkv=0) == pp.PP_ERR_INVALID_ARG
     assert call(scale=float("nan")) == pp.PP_ERR_INVALID_ARG
     assert call(k=K + 2) == pp.PP_ERR_INVALID_ARG             # misaligned
     assert call(out=V + 1024) == pp.PP_ERR_INVALID_ARG        # out overlaps an input

@@ -101,3 +101,24 @@ def test_prefill_single_slot(first_id):
     out = _run(case)
     # one visible key (itself): the output is its value
     assert torch.equal(out.cpu(), case.v)
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,dtype", [(8, 2, 128, torch.bfloat16), (7, 1, 64, torch.bfloat16),
+                                          (4, 2, 64, torch.float32)])
+def test_prefill_grouped_heads(Hq, Hkv, D, dtype):
+    case = prefill_case(Hq, D, 650, _rng_lens(Hq, 9, 1, 40), dtype=dtype, seed=Hq * 3, shuffle_tail=True,
+                        name=f"gqa{Hq}x{Hkv}", Hkv=Hkv)
+    out = _run(case)
+    assert_close(out[: case.seq_len], _ref(case), what=f"prefill {Hq}/{Hkv} heads")
+
+
+def test_prefill_grouped_heads_full_size_sampled():
+    # the 16k-token document with 256 questions, 28 query heads sharing 4
+    case = prefill_case(28, 128, 16384, _rng_lens(1, 256, 8, 48), seed=1009, name="qwen_shape_prefill", Hkv=4)
+    T, doc = case.seq_len, case.doc_len
+    out = _run(case)
+    rows = sorted({0, 255, 256, doc - 1, doc, doc + 1, (doc + T) // 2, T - 1} |
+                  set(np.random.default_rng(2).choice(T, 8, replace=False).tolist()))
+    ref = _ref(case, rows=rows)
+    assert_close(out[rows], ref[rows], what="prefill 28/4 heads, 16k document")
+

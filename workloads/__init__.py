@@ -325,10 +325,11 @@ class PrefillCase:
 
 def prefill_case(H: int, D: int, doc_len: int, q_lens: Sequence[int], dtype: torch.dtype = torch.bfloat16,
                  seed: int = 0, a_lens: Optional[Sequence[int]] = None, shuffle_tail: bool = False,
-                 name: str = "") -> PrefillCase:
+                 name: str = "", Hkv: Optional[int] = None) -> PrefillCase:
     """The packed request before decoding: the document, then each stream's
-    question (and, if given, answer tokens), Q/K/V ~ N(0,1) for every slot.
-    shuffle_tail permutes the slots after the document (ids with them)."""
+    question (and, if given, answer tokens), Q/K/V ~ N(0,1) for every slot
+    (H query heads; K/V with Hkv heads, default H).  shuffle_tail permutes
+    the slots after the document (ids with them)."""
     a = [0] * len(q_lens) if a_lens is None else a_lens
     ids, _ = canonical_layout(doc_len, q_lens, a)
     rng = np.random.Generator(np.random.PCG64(seed))
@@ -337,9 +338,10 @@ def prefill_case(H: int, D: int, doc_len: int, q_lens: Sequence[int], dtype: tor
         rng.shuffle(tail)
         ids = np.concatenate([ids[:doc_len], tail]).astype(np.int32)
     T = int(ids.shape[0])
+    hk = H if Hkv is None else Hkv
     q = rng.standard_normal((T, H, D), dtype=np.float32)
-    k = rng.standard_normal((T, H, D), dtype=np.float32)
-    v = rng.standard_normal((T, H, D), dtype=np.float32)
+    k = rng.standard_normal((T, hk, D), dtype=np.float32)
+    v = rng.standard_normal((T, hk, D), dtype=np.float32)
     return PrefillCase(q=_round(q, dtype), k=_round(k, dtype), v=_round(v, dtype), stream_id=torch.from_numpy(ids),
                        seq_len=T, doc_len=doc_len, H=H, D=D, scale=1.0 / math.sqrt(D), name=name)
 
