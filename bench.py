@@ -174,36 +174,39 @@ def copy_calibration(steps: int):
 
 
 def decode_loop(torch, pp, dev, layers=32, steps=32, doc=12000, P=256, H=32, D=128, seed=1003, rope_base=1e6,
-                with_oracle=True):
+                with_oracle=True, Hkv=None, model="codellama7b"):
     """The answer loop of a 12000-token document with 256 streams: 32 steps of
     32 layers, each step appending one slot per stream (ids and plan once per
     step, then per layer: rotary embedding at the shared positions, append,
     attention).  Timed eagerly and as one captured HIP graph of the step
     replayed every step (the step's start lives on the device).  The q/k/v
     inputs of a layer are reused from step to step here (values do not change
-    the work); the parity tests use fresh ones."""
+    the work); the parity tests use fresh ones.  Hkv < H: query heads in
+    groups sharing a key/value head."""
     from workloads import decode_loop_layout
 
+    Hkv = H if Hkv is None else Hkv
     ids_full, q_lens, base0 = decode_loop_layout(doc, P, steps, seed)
     cap = len(ids_full)
     ids = ids_full.copy()
     ids[base0:] = 0
     sid = torch.from_numpy(ids).to(dev)
     g = torch.Generator(device=dev).manual_seed(seed)
-    K = torch.randn(layers, cap, H, D, generator=g, device=dev, dtype=torch.bfloat16)
-    V = torch.randn(layers, cap, H, D, generator=g, device=dev, dtype=torch.bfloat16)
-    qkv = torch.randn(layers, 3, P, H, D, generator=g, device=dev, dtype=torch.bfloat16)
+    K = torch.randn(layers, cap, Hkv, D, generator=g, device=dev, dtype=torch.bfloat16)
+    V = torch.randn(layers, cap, Hkv, D, generator=g, device=dev, dtype=torch.bfloat16)
+    qs = torch.randn(layers, P, H, D, generator=g, device=dev, dtype=torch.bfloat16)
+    kvn = torch.randn(layers, 2, P, Hkv, D, generator=g, device=dev, dtype=torch.bfloat16)
     outs = torch.empty(layers, P, H, D, device=dev, dtype=torch.bfloat16)
     base = torch.tensor([base0], dtype=torch.int32, device=dev)
     plan = (torch.zeros(2, dtype=torch.int32, device=dev), torch.zeros(P, dtype=torch.int32, device=dev),
             torch.zeros(P, 256, dtype=torch.int32, device=dev))
-    ws = torch.empty(pp.workspace_bytes(cap, P, H, D, torch.bfloat16), dtype=torch.uint8, device=dev)
+    ws = torch.empty(pp.multi_workspace_bytes(cap, 1, P, H, Hkv, D, torch.bfloat16), dtype=torch.uint8, device=dev)
     scale = 1.0 / math.sqrt(D)
 
     def one_step():
         pp.pp_step_plan(sid, base, P, max_seq_len=cap, plan=plan)
         for i in range(layers):
-            pp.pp_attn_decode_append(qkv[i, 0], qkv[i, 1], qkv[i, 2], K[i], V[i], sid, plan, scale=scale,
+            pp.pp_attn_decode_append(qs[i], kvn[i, 0], kvn[i, 1], K[i], V[i], sid, plan, scale=scale,
                                      rope_base=rope_base, out=outs[i], workspace=ws, max_seq_len=cap)
         base.add_(P)
 
@@ -234,7 +237,7 @@ def decode_loop(torch, pp, dev, layers=32, steps=32, doc=12000, P=256, H=32, D=1
 
         b_last = base0 + (steps - 1) * P
         kc, vc = K[0, :b_last + P].cpu(), V[0, :b_last + P].cpu()
-        qi, ki, vi = (x.cpu() for x in (qkv[0, 0], qkv[0, 1], qkv[0, 2]))
+        qi, ki, vi = (x.cpu() for x in (qs[0], kvn[0, 0], kvn[0, 1]))
         cpu = oracle_rate(lambda: oracle_append_step(qi, ki, vi, kc, vc, ids_full, b_last, scale, rope_base,
                                                      streams=[0, 85, 170, 255]),
                           4 / layers, "answer tok/s",
@@ -243,10 +246,11 @@ def decode_loop(torch, pp, dev, layers=32, steps=32, doc=12000, P=256, H=32, D=1
     # KV bytes the loop reads: every layer-step reads the document and each
     # stream's own slots (its question and the answers so far, new one included)
     tail_slots = sum(sum(q_lens) + P * (t + 1) for t in range(steps))
-    kv_bytes = layers * (steps * doc + tail_slots) * H * D * 2 * 2
+    kv_bytes = layers * (steps * doc + tail_slots) * Hkv * D * 2 * 2
+    attn_flops = layers * (steps * P * doc + tail_slots) * H * D * 4
     return {
-        "workload": f"codellama7b_doc12k_p{P}_{layers}layers_{steps}steps",
-        "layers": layers, "steps": steps, "P": P, "doc_len": doc, "rope_base": rope_base,
+        "workload": f"{model}_doc12k_p{P}_{layers}layers_{steps}steps",
+        "layers": layers, "steps": steps, "P": P, "doc_len": doc, "rope_base": rope_base, "Hq": H, "Hkv": Hkv,
         "seq_len_first_last": [base0 + P, base0 + steps * P],
         "graph_ms_total": graph_ms, "eager_ms_total": eager_ms,
         "graph_ms_per_step": graph_ms / steps, "eager_ms_per_step": eager_ms / steps,
@@ -254,6 +258,11 @@ def decode_loop(torch, pp, dev, layers=32, steps=32, doc=12000, P=256, H=32, D=1
         "answer_tok_s_graph": P * steps / (graph_ms / 1e3),
         "effective_kv_gbs_graph": kv_bytes / (graph_ms / 1e3) / 1e9,
         "effective_kv_hbm_frac_graph": kv_bytes / (graph_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+        # with grouped heads every K/V row meets Hq / Hkv queries, so the
+        # loop leans on the matrix cores: its attention flops (QK and PV,
+        # 2 flops per multiply-add) against the dense bf16 peak
+        "attn_tflops_graph": attn_flops / (graph_ms / 1e3) / 1e12,
+        "attn_mfma_frac_graph": attn_flops / (graph_ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
         "inputs": "per-layer q/k/v reused across steps; caches N(0,1) bf16 from a seeded device generator",
         "cpu_oracle": cpu,
     }
@@ -643,6 +652,10 @@ def main():
     if not args.no_decode_loop:
         log("bench: 32-step x 32-layer appending loop")
         loop = decode_loop(torch, pp, dev, with_oracle=not args.no_cpu_baseline)
+        torch.cuda.empty_cache()
+        log("bench: appending loop, 28 query heads sharing 4 key/value heads")
+        loop["grouped_heads"] = decode_loop(torch, pp, dev, layers=28, H=28, Hkv=4, with_oracle=False,
+                                            model="qwen7b_shape")
         torch.cuda.empty_cache()
 
     sweep = None

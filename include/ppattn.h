@@ -232,19 +232,24 @@ pp_status_t pp_step_plan(int32_t* stream_id, const int32_t* base_len, int64_t ma
  *   `dtype`
  *   k_cache[j_s] = rotated k_new[s];  v_cache[j_s] = v_new[s]
  *   out = pp_attn_decode_planned(rotated q, k_cache, v_cache, stream_id,
- *                                seq_len, ...)  with the step's plan.
- *   q, k_new, v_new  [P, H, d] element type `dtype`, device, read only
- *   k_cache, v_cache [max_seq_len, H, d], device, rows j_s written
+ *                                seq_len, ...)  with the step's plan, query
+ *         head h reading key/value head h / (Hq / Hkv).
+ *   q                [P, Hq, d] element type `dtype`, device, read only
+ *   k_new, v_new     [P, Hkv, d], device, read only
+ *   k_cache, v_cache [max_seq_len, Hkv, d], device, rows j_s written
+ *   out              [P, Hq, d]
  *   max_seq_len      host bound of every step's seq_len (sizes the caches,
- *                    stream_id and the workspace: pp_attn_workspace_bytes(
- *                    max_seq_len, P, H, d, dtype))
- * The caches must not overlap each other or any other argument; k_new and
- * v_new must not overlap out or the workspace (PP_ERR_INVALID_ARG); rope_base
- * must be finite.  Other arguments, results and errors as
- * pp_attn_decode_planned. */
+ *                    stream_id and the workspace: pp_attn_multi_workspace_bytes(
+ *                    max_seq_len, 1, P, Hq, Hkv, d, dtype), which is
+ *                    pp_attn_workspace_bytes(max_seq_len, P, Hq, d, dtype)
+ *                    when Hq == Hkv)
+ * Hq must be a multiple of Hkv.  The caches must not overlap each other or
+ * any other argument; k_new and v_new must not overlap out or the workspace
+ * (PP_ERR_INVALID_ARG); rope_base must be finite.  Other arguments, results
+ * and errors as pp_attn_decode_planned. */
 pp_status_t pp_attn_decode_append(const void* q, const void* k_new, const void* v_new, void* k_cache,
                                   void* v_cache, const int32_t* stream_id, int64_t max_seq_len, int32_t P,
-                                  int32_t H, int32_t d, float scale, double rope_base,
+                                  int32_t Hq, int32_t Hkv, int32_t d, float scale, double rope_base,
                                   const int32_t* plan_head, const int32_t* plan_counts,
                                   const int32_t* plan_slots, int64_t plan_capacity, void* out,
                                   pp_dtype_t dtype, void* workspace, size_t workspace_bytes,

@@ -100,8 +100,10 @@ def oracle_append_step(q, k_new, v_new, k_cache, v_cache, stream_id, base_len: i
     the key and the value are stored in the cache, and every stream attends
     over the first base_len + P slots.
 
-    q, k_new, v_new: [P, H, d]; k_cache, v_cache: [T >= base_len + P, H, d]
-    (the first base_len slots hold earlier, already rotated keys); stream_id:
+    q: [P, Hq, d]; k_new, v_new: [P, Hkv, d]; k_cache, v_cache: [T >=
+    base_len + P, Hkv, d], Hq a multiple of Hkv, query head h reading
+    key/value head h // (Hq // Hkv) (the first base_len slots hold earlier,
+    already rotated keys); stream_id:
     [T] (slots >= base_len are overwritten).  With store_bf16 the rotated
     query and key and the stored value are rounded to bf16 (the caches'
     element type), else kept in float64.

@@ -111,8 +111,8 @@ def _load():
     lib.pp_step_plan.restype = ctypes.c_int
     lib.pp_step_plan.argtypes = [vp, vp, i64, i32, vp, vp, vp, i64, vp]
     lib.pp_attn_decode_append.restype = ctypes.c_int
-    lib.pp_attn_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, f32, ctypes.c_double, vp, vp,
-                                          vp, i64, vp, ctypes.c_int, vp, sz, vp]
+    lib.pp_attn_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, f32, ctypes.c_double, vp,
+                                          vp, vp, i64, vp, ctypes.c_int, vp, sz, vp]
     lib.pp_attn_prefill_workspace_bytes.restype = sz
     lib.pp_attn_prefill_workspace_bytes.argtypes = [i64, i32, i32, ctypes.c_int]
     lib.pp_attn_prefill.restype = ctypes.c_int
@@ -344,18 +344,42 @@ def pp_attn_decode_append(q, k_new, v_new, k_cache, v_cache, stream_id, plan, sc
     """One layer of a step started by pp_step_plan: the new keys and values
     go into the caches (keys and queries rotated at the streams' shared
     positions; rope_base <= 0 switches the rotation off), then the decode
-    attention over the step's seq_len.  Returns `out` without synchronising."""
+    attention over the step's seq_len.  q [P, Hq, d]; k_new, v_new [P, Hkv,
+    d]; k_cache, v_cache [T, Hkv, d] (Hq a multiple of Hkv).  Returns `out`
+    [P, Hq, d] without synchronising."""
     import torch
 
-    if max_seq_len is None:
-        max_seq_len = min(k_cache.shape[0], stream_id.numel()) if k_cache.dim() == 3 else 0
-    P, H, d, max_seq_len, scale, code, out, workspace = _prepare(q, k_cache, v_cache, stream_id, max_seq_len, scale,
-                                                                 out, workspace)
-    for name, t in (("k_new", k_new), ("v_new", v_new)):
+    for name, t in (("q", q), ("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache), ("v_cache", v_cache),
+                    ("stream_id", stream_id)):
         if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous GPU tensor")
-        if t.shape != q.shape or t.dtype != q.dtype:
-            raise ValueError(f"{name} must be shaped and typed like q")
+    if q.dim() != 3 or k_cache.dim() != 3 or k_cache.shape != v_cache.shape:
+        raise ValueError("q must be [P, Hq, d] and k_cache, v_cache [T, Hkv, d]")
+    P, H, d = q.shape
+    T, Hkv, dk = k_cache.shape
+    if dk != d:
+        raise ValueError(f"k_cache {tuple(k_cache.shape)} does not match q {tuple(q.shape)}")
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if tuple(t.shape) != (P, Hkv, d):
+            raise ValueError(f"{name} must be [P, Hkv, d] = {(P, Hkv, d)}, got {tuple(t.shape)}")
+    if not (q.dtype == k_new.dtype == v_new.dtype == k_cache.dtype == v_cache.dtype):
+        raise ValueError("q, k_new, v_new, k_cache and v_cache must share one dtype")
+    if stream_id.dtype != torch.int32 or stream_id.dim() != 1:
+        raise ValueError("stream_id must be a 1-D int32 tensor")
+    if max_seq_len is None:
+        max_seq_len = min(T, stream_id.numel())
+    max_seq_len = int(max_seq_len)
+    if not (1 <= max_seq_len <= T) or stream_id.numel() < max_seq_len:
+        raise ValueError(f"max_seq_len={max_seq_len} must be in [1, {T}] and <= len(stream_id)")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    code = _dtype_code(q.dtype)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_cuda or not out.is_contiguous():
+        raise ValueError("out must be a contiguous GPU tensor shaped and typed like q")
+    if workspace is None:
+        workspace = torch.empty(multi_workspace_bytes(max_seq_len, 1, P, H, Hkv, d, code), dtype=torch.uint8,
+                                device=q.device)
     head, counts, slots = plan
     for name, t in (("head", head), ("counts", counts), ("slots", slots)):
         if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.int32:
@@ -367,7 +391,7 @@ def pp_attn_decode_append(q, k_new, v_new, k_cache, v_cache, stream_id, plan, sc
         raise ValueError("plan slots must be contiguous")
     st = _load().pp_attn_decode_append(
         q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-        stream_id.data_ptr(), max_seq_len, P, H, d, scale, float(rope_base), head.data_ptr(), counts.data_ptr(),
+        stream_id.data_ptr(), max_seq_len, P, H, Hkv, d, scale, float(rope_base), head.data_ptr(), counts.data_ptr(),
         slots.data_ptr() if cap > 0 else None, cap, out.data_ptr(), code, workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _stream_handle(q.device))
     _check(st)

@@ -109,9 +109,9 @@ struct AppendArgs {
   double rope_base;
 };
 
-// bt (several requests, grouped key/value heads) comes with the multi entry
-// points only, which have checked B, G and seq_lens; H is the number of
-// query heads.
+// bt (several requests, grouped key/value heads) comes with the multi and
+// appending entry points only, which have checked B, G and seq_lens; H is
+// the number of query heads.
 pp_status_t decode_impl(Path path, const void* q, const void* k, const void* v, const int32_t* sid, int64_t seq_len,
                         int32_t P, int32_t H, int32_t d, float scale, void* out, pp_dtype_t dtype, void* workspace,
                         size_t workspace_bytes, void* hip_stream, void* const* events = nullptr,
@@ -155,15 +155,16 @@ pp_status_t decode_impl(Path path, const void* q, const void* k, const void* v, 
       return fail(PP_ERR_INVALID_ARG, "k_new and v_new must be 16-byte aligned");
     if (!isfinite(ap->rope_base)) return fail(PP_ERR_INVALID_ARG, "rope_base is not finite");
     // the caches are written: nothing read in the step may share their bytes
+    const size_t nn = (size_t)P * Hkv * d * es;  // new keys (values) of the step
     for (const void* w : {k, v})
-      if (overlaps(w, nkv, q, nq) || overlaps(w, nkv, ap->k_new, nq) || overlaps(w, nkv, ap->v_new, nq) ||
+      if (overlaps(w, nkv, q, nq) || overlaps(w, nkv, ap->k_new, nn) || overlaps(w, nkv, ap->v_new, nn) ||
           overlaps(w, nkv, sid, nid) || overlaps(w, nkv, workspace, workspace_bytes) ||
           overlaps(w, nkv, xp->doc_len, 8) || overlaps(w, nkv, xp->counts, (size_t)P * 4) ||
           overlaps(w, nkv, xp->slots, (size_t)P * (size_t)(xp->capacity > 0 ? xp->capacity : 0) * 4))
         return fail(PP_ERR_INVALID_ARG, "k_cache or v_cache overlaps another argument");
     if (overlaps(k, nkv, v, nkv)) return fail(PP_ERR_INVALID_ARG, "k_cache and v_cache overlap");
-    if (overlaps(out, nq, ap->k_new, nq) || overlaps(out, nq, ap->v_new, nq) ||
-        overlaps(workspace, workspace_bytes, ap->k_new, nq) || overlaps(workspace, workspace_bytes, ap->v_new, nq))
+    if (overlaps(out, nq, ap->k_new, nn) || overlaps(out, nq, ap->v_new, nn) ||
+        overlaps(workspace, workspace_bytes, ap->k_new, nn) || overlaps(workspace, workspace_bytes, ap->v_new, nn))
       return fail(PP_ERR_INVALID_ARG, "k_new or v_new overlaps out or the workspace");
   }
   const size_t need = required_bytes(seq_len, P, H, d, dtype, B, G);
@@ -194,7 +195,7 @@ pp_status_t decode_impl(Path path, const void* q, const void* k, const void* v, 
   hipError_t e = mark(0);
   if (e == hipSuccess && !xp) e = pp::launch_plan(sid, seq_len, P, ws.plan, ws.counts, ws.slots, ws.cap, stream, bt);
   if (e == hipSuccess && ap) {  // new keys and values into the caches, rotated queries into the workspace
-    e = pp::launch_append_rope(q, ap->k_new, ap->v_new, const_cast<void*>(k), const_cast<void*>(v), P, H, d, dtype,
+    e = pp::launch_append_rope(q, ap->k_new, ap->v_new, const_cast<void*>(k), const_cast<void*>(v), P, H, Hkv, d, dtype,
                                ap->rope_base, ws.plan, ws.counts, seq_len, ws.q_rot, stream);
     q = ws.q_rot;
   }
@@ -321,14 +322,18 @@ pp_status_t pp_step_plan(int32_t* stream_id, const int32_t* base_len, int64_t ma
 }
 
 pp_status_t pp_attn_decode_append(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
-                                  const int32_t* stream_id, int64_t max_seq_len, int32_t P, int32_t H, int32_t d,
-                                  float scale, double rope_base, const int32_t* plan_head, const int32_t* plan_counts,
-                                  const int32_t* plan_slots, int64_t plan_capacity, void* out, pp_dtype_t dtype,
-                                  void* workspace, size_t workspace_bytes, void* hip_stream) {
+                                  const int32_t* stream_id, int64_t max_seq_len, int32_t P, int32_t Hq, int32_t Hkv,
+                                  int32_t d, float scale, double rope_base, const int32_t* plan_head,
+                                  const int32_t* plan_counts, const int32_t* plan_slots, int64_t plan_capacity,
+                                  void* out, pp_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                  void* hip_stream) {
+  if (Hkv < 1 || Hq % Hkv != 0) return fail(PP_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
   const ExternalPlan xp{plan_head, plan_counts, plan_slots, plan_capacity};
   const AppendArgs ap{k_new, v_new, rope_base};
-  return decode_impl(Path::kParallel, q, k_cache, v_cache, stream_id, max_seq_len, P, H, d, scale, out, dtype,
-                     workspace, workspace_bytes, hip_stream, nullptr, &xp, &ap);
+  pp::Batch bt;
+  bt.G = Hq / Hkv;
+  return decode_impl(Path::kParallel, q, k_cache, v_cache, stream_id, max_seq_len, P, Hq, d, scale, out, dtype,
+                     workspace, workspace_bytes, hip_stream, nullptr, &xp, &ap, bt);
 }
 
 size_t pp_attn_multi_workspace_bytes(int64_t max_seq_len, int32_t B, int32_t P, int32_t Hq, int32_t Hkv, int32_t d,

@@ -309,7 +309,7 @@ hipError_t launch_plan_append(int32_t* sid, const int32_t* base_len, int64_t max
 // cache slots [seq_len - P, seq_len); the rotated queries go to q_rot.
 // rope_base <= 0: no rotation.
 hipError_t launch_append_rope(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
-                              int P, int H, int d, pp_dtype_t dtype, double rope_base, const int32_t* plan,
+                              int P, int Hq, int Hkv, int d, pp_dtype_t dtype, double rope_base, const int32_t* plan,
                               const int32_t* counts, int64_t max_len, void* q_rot, hipStream_t stream);
 
 // Document part, all P queries of a head at once: split-K partial softmax

@@ -57,11 +57,13 @@ __device__ __forceinline__ void store4<float>(float* p, const float* f) {
 
 // plan = {doc_len, seq_len} of the step (from the appending plan kernel);
 // the step's new slots are [seq_len - P, seq_len).  An empty or out-of-range
-// plan writes nothing.
+// plan writes nothing.  Hq query heads, Hkv key/value heads (Hq = Hkv
+// without grouping): the queries have Hq rows per stream, the new keys and
+// values Hkv.
 template <typename T, int D>
 __global__ __launch_bounds__(kAppendThreads) void append_rope_kernel(
     const T* __restrict__ q, const T* __restrict__ k_new, const T* __restrict__ v_new, T* __restrict__ k_cache,
-    T* __restrict__ v_cache, int H, double rope_base, const int32_t* __restrict__ plan,
+    T* __restrict__ v_cache, int Hq, int Hkv, double rope_base, const int32_t* __restrict__ plan,
     const int32_t* __restrict__ counts, int64_t max_len, T* __restrict__ q_rot) {
   constexpr int HALF = D / 2;
   constexpr int C4 = HALF / 4;  // chunks of 4 pairs per head
@@ -82,46 +84,45 @@ __global__ __launch_bounds__(kAppendThreads) void append_rope_kernel(
     }
     __syncthreads();
   }
-  const int64_t qoff = (int64_t)s * H * D, koff = slot * H * D;
-  for (int it = tid; it < H * C4; it += kAppendThreads) {
-    const int h = it / C4, i0 = (it % C4) * 4;
-    const int64_t lo = (int64_t)h * D + i0, hi = lo + HALF;
-    float qa[4], qb[4], ka[4], kb[4];
-    load4<T>(q + qoff + lo, qa);
-    load4<T>(q + qoff + hi, qb);
-    load4<T>(k_new + qoff + lo, ka);
-    load4<T>(k_new + qoff + hi, kb);
-    if (rot) {
+  // rows [0, nh) of D elements from src, each pair (i, i + D/2) rotated, to dst
+  auto rotate = [&](const T* src, T* dst, int nh) {
+    for (int it = tid; it < nh * C4; it += kAppendThreads) {
+      const int h = it / C4, i0 = (it % C4) * 4;
+      const int64_t lo = (int64_t)h * D + i0, hi = lo + HALF;
+      float a[4], b4[4];
+      load4<T>(src + lo, a);
+      load4<T>(src + hi, b4);
+      if (rot) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float c = cs[i0 + e], sv = sn[i0 + e];
-        const float x = qa[e], y = qb[e], u = ka[e], w = kb[e];
-        qa[e] = fmaf(x, c, -y * sv);
-        qb[e] = fmaf(y, c, x * sv);
-        ka[e] = fmaf(u, c, -w * sv);
-        kb[e] = fmaf(w, c, u * sv);
+        for (int e = 0; e < 4; ++e) {
+          const float c = cs[i0 + e], sv = sn[i0 + e];
+          const float x = a[e], y = b4[e];
+          a[e] = fmaf(x, c, -y * sv);
+          b4[e] = fmaf(y, c, x * sv);
+        }
       }
+      store4<T>(dst + lo, a);
+      store4<T>(dst + hi, b4);
     }
-    store4<T>(q_rot + qoff + lo, qa);
-    store4<T>(q_rot + qoff + hi, qb);
-    store4<T>(k_cache + koff + lo, ka);
-    store4<T>(k_cache + koff + hi, kb);
-  }
+  };
+  const int64_t qoff = (int64_t)s * Hq * D, knoff = (int64_t)s * Hkv * D, koff = slot * Hkv * D;
+  rotate(q + qoff, q_rot + qoff, Hq);
+  rotate(k_new + knoff, k_cache + koff, Hkv);
   constexpr int VE = 16 / (int)sizeof(T);  // elements per 16-byte vector
-  for (int it = tid; it < H * D / VE; it += kAppendThreads)
+  for (int it = tid; it < Hkv * D / VE; it += kAppendThreads)
     *reinterpret_cast<u32x4*>(v_cache + koff + (int64_t)it * VE) =
-        *reinterpret_cast<const u32x4*>(v_new + qoff + (int64_t)it * VE);
+        *reinterpret_cast<const u32x4*>(v_new + knoff + (int64_t)it * VE);
 }
 
 }  // namespace
 
 hipError_t launch_append_rope(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
-                              int P, int H, int d, pp_dtype_t dtype, double rope_base, const int32_t* plan,
+                              int P, int Hq, int Hkv, int d, pp_dtype_t dtype, double rope_base, const int32_t* plan,
                               const int32_t* counts, int64_t max_len, void* q_rot, hipStream_t stream) {
 #define PP_APPEND_LAUNCH(TT, DD)                                                                              \
   append_rope_kernel<TT, DD><<<P, kAppendThreads, 0, stream>>>(                                               \
       static_cast<const TT*>(q), static_cast<const TT*>(k_new), static_cast<const TT*>(v_new),                \
-      static_cast<TT*>(k_cache), static_cast<TT*>(v_cache), H, rope_base, plan, counts, max_len,              \
+      static_cast<TT*>(k_cache), static_cast<TT*>(v_cache), Hq, Hkv, rope_base, plan, counts, max_len,       \
       static_cast<TT*>(q_rot))
   if (dtype == PP_BF16) {
     if (d == 128) PP_APPEND_LAUNCH(uint16_t, 128);

@@ -175,9 +175,10 @@ def test_decode_append_validation():
     KN, VN, HEAD, CNT, SL = 0x70000000, 0x78000000, 0x80000000, 0x90000000, 0xA0000000
     ws_bytes = lib.pp_attn_workspace_bytes(1000, 8, 4, 128, pp.PP_BF16)
 
-    def call(q=Q, kn=KN, vn=VN, k=K, v=V, max_len=1000, P=8, rope=1e4, out=OUT, head=HEAD, ws=WS, wsb=ws_bytes):
-        return lib.pp_attn_decode_append(q, kn, vn, k, v, SID, max_len, P, 4, 128, 0.088, rope, head, CNT, SL, 16, out,
-                                         pp.PP_BF16, ws, wsb, None)
+    def call(q=Q, kn=KN, vn=VN, k=K, v=V, max_len=1000, P=8, rope=1e4, out=OUT, head=HEAD, ws=WS, wsb=ws_bytes,
+             Hq=4, Hkv=4):
+        return lib.pp_attn_decode_append(q, kn, vn, k, v, SID, max_len, P, Hq, Hkv, 128, 0.088, rope, head, CNT, SL,
+                                         16, out, pp.PP_BF16, ws, wsb, None)
 
     assert call(kn=None) == pp.PP_ERR_INVALID_ARG
     assert call(vn=VN + 8) == pp.PP_ERR_INVALID_ARG            # misaligned
@@ -193,6 +194,15 @@ def test_decode_append_validation():
     assert call(P=0) == pp.PP_ERR_INVALID_ARG
     assert call(max_len=6, wsb=1 << 30) == pp.PP_ERR_INVALID_ARG  # P > max_seq_len
     assert call(wsb=1024) == pp.PP_ERR_WORKSPACE
+    assert call(Hkv=3) == pp.PP_ERR_INVALID_ARG                # 4 query heads are not a multiple of 3
+    assert call(Hkv=0) == pp.PP_ERR_INVALID_ARG
+    # grouped heads: the caches and the new keys hold Hkv = 1 row per slot,
+    # and the workspace is the grouped one
+    gq_bytes = lib.pp_attn_multi_workspace_bytes(1000, 1, 8, 4, 1, 128, pp.PP_BF16)
+    assert gq_bytes > 0
+    assert call(v=K + 1000 * 128 * 2, Hkv=1, wsb=gq_bytes - 1) == pp.PP_ERR_WORKSPACE
+    assert call(v=K + 1000 * 128 * 2 - 256, Hkv=1, wsb=gq_bytes) == pp.PP_ERR_INVALID_ARG  # caches overlap
+    assert call(kn=OUT - 8 * 128 * 2 + 16, Hkv=1, wsb=gq_bytes) == pp.PP_ERR_INVALID_ARG  # one-row key ends in out
     assert lib.pp_last_error_message().decode() != ""
 
 

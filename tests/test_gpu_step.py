@@ -96,15 +96,17 @@ def test_step_plan_out_of_range_base_is_an_empty_step(base):
 
 # ------------------------------------------------- append + rotate + attend ---
 
-def _step_case(seed, P, H, D, doc, dtype):
+def _step_case(seed, P, H, D, doc, dtype, Hkv=None):
+    Hkv = H if Hkv is None else Hkv
     rng = np.random.default_rng(seed)
     ids0, _ = canonical_layout(doc, rng.integers(1, 40, P).tolist(), rng.integers(0, 12, P).tolist())
     T0 = len(ids0)
     cap = T0 + P + 5
     g = torch.Generator().manual_seed(seed)
-    k = torch.randn(cap, H, D, generator=g).to(dtype)
-    v = torch.randn(cap, H, D, generator=g).to(dtype)
-    q, kn, vn = (torch.randn(P, H, D, generator=g).to(dtype) for _ in range(3))
+    k = torch.randn(cap, Hkv, D, generator=g).to(dtype)
+    v = torch.randn(cap, Hkv, D, generator=g).to(dtype)
+    q = torch.randn(P, H, D, generator=g).to(dtype)
+    kn, vn = (torch.randn(P, Hkv, D, generator=g).to(dtype) for _ in range(2))
     ids = np.concatenate([ids0, np.full(cap - T0, 0, dtype=np.int32)])
     return ids, T0, cap, k, v, q, kn, vn
 
@@ -160,7 +162,7 @@ def test_decode_append_without_rotation_equals_append_then_decode():
 
 # ------------------------------------------- graph of a multi-layer step ---
 
-def _loop(doc, P, steps, layers, H, D, seed, rope_base, check_oracle, use_graph):
+def _loop(doc, P, steps, layers, H, D, seed, rope_base, check_oracle, use_graph, Hkv=None):
     """32-step style loop: at every step each stream appends one slot and
     every layer attends.  Returns the per-(step, layer) outputs on the host
     and, with check_oracle, compares each with the step oracle's own loop."""
@@ -170,24 +172,25 @@ def _loop(doc, P, steps, layers, H, D, seed, rope_base, check_oracle, use_graph)
     ids = ids_full.copy()
     ids[base0:] = 0  # the appended region holds stale ids until a step writes them
     sid = _i32(ids)
-    K = [torch.empty(cap, H, D, dtype=torch.bfloat16, device=DEV) for _ in layers]
+    Hkv = H if Hkv is None else Hkv
+    K = [torch.empty(cap, Hkv, D, dtype=torch.bfloat16, device=DEV) for _ in layers]
     V = [torch.empty_like(K[0]) for _ in layers]
     oK, oV = [], []
     for i, layer in enumerate(layers):
-        inp = decode_loop_step_inputs(H, D, P, cap, layer, 0, seed, base_len=base0)
+        inp = decode_loop_step_inputs(H, D, P, cap, layer, 0, seed, base_len=base0, Hkv=Hkv)
         K[i][:base0] = inp["k0"].to(DEV)
         V[i][:base0] = inp["v0"].to(DEV)
         if check_oracle:
-            oK.append(np.zeros((cap, H, D)))
-            oV.append(np.zeros((cap, H, D)))
+            oK.append(np.zeros((cap, Hkv, D)))
+            oV.append(np.zeros((cap, Hkv, D)))
             oK[i][:base0] = inp["k0"].double().numpy()
             oV[i][:base0] = inp["v0"].double().numpy()
     o_ids = ids.copy()
     base = _i32([base0])
     plan = (torch.zeros(2, dtype=torch.int32, device=DEV), torch.zeros(P, dtype=torch.int32, device=DEV),
             torch.zeros(P, 256, dtype=torch.int32, device=DEV))
-    ws = torch.empty(pp.workspace_bytes(cap, P, H, D, torch.bfloat16), dtype=torch.uint8, device=DEV)
-    qin = [torch.empty(P, H, D, dtype=torch.bfloat16, device=DEV) for _ in range(3 * len(layers))]
+    ws = torch.empty(pp.multi_workspace_bytes(cap, 1, P, H, Hkv, D, torch.bfloat16), dtype=torch.uint8, device=DEV)
+    qin = [torch.empty(P, h, D, dtype=torch.bfloat16, device=DEV) for _ in layers for h in (H, Hkv, Hkv)]
     outs = [torch.empty(P, H, D, dtype=torch.bfloat16, device=DEV) for _ in layers]
 
     def step():
@@ -208,7 +211,7 @@ def _loop(doc, P, steps, layers, H, D, seed, rope_base, check_oracle, use_graph)
         base.fill_(base0)  # capture does not run the work
     results = []
     for t in range(steps):
-        inps = [decode_loop_step_inputs(H, D, P, cap, layer, t, seed, base_len=base0) for layer in layers]
+        inps = [decode_loop_step_inputs(H, D, P, cap, layer, t, seed, base_len=base0, Hkv=Hkv) for layer in layers]
         for i, inp in enumerate(inps):
             qin[3 * i].copy_(inp["q"])
             qin[3 * i + 1].copy_(inp["k_new"])
@@ -294,3 +297,47 @@ def test_decode_append_stream_counts(P):
     torch.cuda.synchronize()
     r = oracle_append_step(q, kn, vn, k, v, ids, T0, 1.0 / np.sqrt(D), 1e4)
     assert_close(out, r["out"], what=f"appending step P={P}")
+
+
+# ----------------------------------------------- grouped key/value heads ---
+
+@pytest.mark.parametrize("Hq,Hkv,D,dtype,rope_base", [(8, 2, 128, torch.bfloat16, 1e4),
+                                                     (28, 4, 128, torch.bfloat16, 1e6),
+                                                     (7, 1, 64, torch.bfloat16, 1e4),
+                                                     (4, 2, 64, torch.float32, 1e4),
+                                                     (6, 3, 128, torch.bfloat16, 0.0)])
+def test_decode_append_grouped_heads(Hq, Hkv, D, dtype, rope_base):
+    P = 19
+    ids, T0, cap, k, v, q, kn, vn = _step_case(Hq * 13 + Hkv, P, Hq, D, doc=900, dtype=dtype, Hkv=Hkv)
+    kg, vg, sid = k.to(DEV), v.to(DEV), _i32(ids)
+    say(f"  gpu: pp_attn_decode_append grouped Hq={Hq} Hkv={Hkv} {dtype} D={D} base={rope_base} T0={T0} P={P}")
+    plan = pp.pp_step_plan(sid, _i32([T0]), P, max_seq_len=cap)
+    out = pp.pp_attn_decode_append(q.to(DEV), kn.to(DEV), vn.to(DEV), kg, vg, sid, plan, rope_base=rope_base)
+    torch.cuda.synchronize()
+    bf = dtype == torch.bfloat16
+    r = oracle_append_step(q, kn, vn, k, v, ids, T0, 1.0 / np.sqrt(D), rope_base, store_bf16=bf)
+    assert_close(out, r["out"], what=f"grouped {Hq}/{Hkv} {dtype} D={D} base={rope_base}")
+    kw, vw = kg.double().cpu().numpy(), vg.double().cpu().numpy()
+    np.testing.assert_array_equal(kw[:T0], k[:T0].double().numpy())
+    np.testing.assert_array_equal(kw[T0 + P:], k[T0 + P:].double().numpy())
+    np.testing.assert_array_equal(vw[T0:T0 + P], vn.double().numpy())
+    got, want = kw[T0:T0 + P], r["k_rot"]
+    if rope_base <= 0:
+        np.testing.assert_array_equal(got, kn.double().numpy())
+    elif bf:
+        diff = np.abs(got - want)
+        assert (diff <= _rot_bound(want, kn.double().numpy())).all(), diff.max()
+        assert (diff == 0).mean() > 0.99
+    else:
+        np.testing.assert_allclose(got, want, rtol=2e-6, atol=2e-6)
+
+
+def test_graph_of_the_grouped_step_replays_every_step():
+    # 28 query heads sharing 4 key/value heads: one capture of (plan + 2
+    # layers + advance), replayed 12 times, against the oracle's own loop
+    args = dict(doc=700, P=24, steps=12, layers=[0, 1], H=28, Hkv=4, D=128, seed=97, rope_base=1e6)
+    g = _loop(**args, check_oracle=True, use_graph=True)
+    e = _loop(**args, check_oracle=False, use_graph=False)
+    for t in range(len(g)):
+        for i in range(len(g[t])):
+            assert torch.equal(g[t][i].view(torch.int16), e[t][i].view(torch.int16)), (t, i)

@@ -172,6 +172,28 @@ def test_step_without_rotation_is_an_append_then_the_decode():
     assert r["pos"].tolist() == [6 + 2 + 1, 6 + 3 + 0, 6 + 1 + 2]
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(4, 2), (6, 1)])
+def test_grouped_step_equals_the_step_with_heads_repeated(Hq, Hkv):
+    # query head h reads key/value head h // (Hq / Hkv): the grouped step is
+    # the plain step on caches and new keys with each key/value head repeated
+    # for its group of query heads (the rotation acts per head, so repeating
+    # before or after it is the same)
+    rng = np.random.default_rng(Hq * 10 + Hkv)
+    P, d = 3, 8
+    G = Hq // Hkv
+    ids, _ = canonical_layout(5, [2, 1, 3], [1, 2, 0])
+    T0 = len(ids)
+    k, v = rng.standard_normal((T0 + P, Hkv, d)), rng.standard_normal((T0 + P, Hkv, d))
+    q, kn, vn = rng.standard_normal((P, Hq, d)), rng.standard_normal((P, Hkv, d)), rng.standard_normal((P, Hkv, d))
+    sid = np.concatenate([ids, np.zeros(P)]).astype(np.int32)
+    r = oracle_append_step(q, kn, vn, k, v, sid, T0, 0.4, 1e4, store_bf16=False)
+    rep = lambda a: np.repeat(a, G, axis=1)  # noqa: E731
+    full = oracle_append_step(q, rep(kn), rep(vn), rep(k), rep(v), sid, T0, 0.4, 1e4, store_bf16=False)
+    np.testing.assert_allclose(r["out"], full["out"], rtol=1e-13, atol=1e-13)
+    np.testing.assert_array_equal(rep(r["k_rot"]), full["k_rot"])
+    assert r["k_cache"].shape == (T0 + P, Hkv, d)
+
+
 def test_step_rounds_to_bf16_when_asked():
     rng = np.random.default_rng(9)
     P, H, d = 2, 1, 8

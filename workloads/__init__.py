@@ -382,21 +382,24 @@ def decode_loop_layout(doc_len: int, P: int, steps: int, seed: int, q_lo: int = 
 
 
 def decode_loop_step_inputs(H: int, D: int, P: int, capacity: int, layer: int, step: int,
-                            seed: int, dtype=torch.bfloat16, base_len: Optional[int] = None):
+                            seed: int, dtype=torch.bfloat16, base_len: Optional[int] = None,
+                            Hkv: Optional[int] = None):
     """Fresh N(0,1) values for one (layer, step): the step's queries [P,H,D],
-    and, at step 0, the layer's initial cache [base_len,H,D] (K and V);
-    at every step the P appended K/V rows.  Each (layer, step) has its own
-    PCG64 stream, so any sample can be regenerated without the others."""
+    and, at step 0, the layer's initial cache [base_len,Hkv,D] (K and V);
+    at every step the P appended K/V rows [P,Hkv,D] (Hkv defaults to H).
+    Each (layer, step) has its own PCG64 stream, so any sample can be
+    regenerated without the others."""
+    Hkv = H if Hkv is None else Hkv
     rng = np.random.Generator(np.random.PCG64([seed, layer, step]))
     q = rng.standard_normal((P, H, D), dtype=np.float32)
-    k_new = rng.standard_normal((P, H, D), dtype=np.float32)
-    v_new = rng.standard_normal((P, H, D), dtype=np.float32)
+    k_new = rng.standard_normal((P, Hkv, D), dtype=np.float32)
+    v_new = rng.standard_normal((P, Hkv, D), dtype=np.float32)
     out = {"q": _round(q, dtype), "k_new": _round(k_new, dtype), "v_new": _round(v_new, dtype)}
     if step == 0:
         assert base_len is not None
         rng0 = np.random.Generator(np.random.PCG64([seed, layer, 1 << 20]))
-        k0 = rng0.standard_normal((base_len, H, D), dtype=np.float32)
-        v0 = rng0.standard_normal((base_len, H, D), dtype=np.float32)
+        k0 = rng0.standard_normal((base_len, Hkv, D), dtype=np.float32)
+        v0 = rng0.standard_normal((base_len, Hkv, D), dtype=np.float32)
         out["k0"] = _round(k0, dtype)
         out["v0"] = _round(v0, dtype)
     return out
