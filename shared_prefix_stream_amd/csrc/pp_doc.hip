@@ -726,8 +726,14 @@ DocPlan choose_doc_plan(int64_t seq_len, int P, int H, int d, pp_dtype_t dtype, 
     pl.n_ptiles = (P + kDocThreads - 1) / kDocThreads;
     per_cu = 2;
   }
+  // As many splits as fill the resident slots in one round, never more:
+  // with base workgroups per split, a count past floor(slots / base) starts a
+  // second, partly idle round that costs as much as the first (e.g. 28
+  // workgroups per split on 256 CUs: 9 splits, 252 workgroups, one round;
+  // 10 splits would take two rounds of 1/10 of the work).  Monotone in the
+  // CU count, so the workspace sized for 256 CUs covers every device.
   const int64_t base = (int64_t)H * pl.n_ptiles;
-  int64_t want = ((int64_t)num_cus * per_cu + base - 1) / base;
+  int64_t want = ((int64_t)num_cus * per_cu) / base;
   const int64_t max_by_len = (seq_len + 255) / 256;  // at least ~256 slots of the upper bound per split
   if (want > max_by_len) want = max_by_len;
   if (want < 1) want = 1;
