@@ -228,8 +228,8 @@ pp_status_t pp_step_plan(int32_t* stream_id, const int32_t* base_len, int64_t ma
  *            were the only one)
  *   rotary embedding at pos_s of q[s] and k_new[s], rotate-half pairs
  *   (i, i + d/2) turned by pos_s * rope_base^(-2i/d) (rope_base <= 0: no
- *   rotation), angles in double precision, rotation in fp32, one rounding to
- *   `dtype`
+ *   rotation), angles formed and reduced modulo 2*pi in double precision,
+ *   their sine and cosine and the rotation in fp32, one rounding to `dtype`
  *   k_cache[j_s] = rotated k_new[s];  v_cache[j_s] = v_new[s]
  *   out = pp_attn_decode_planned(rotated q, k_cache, v_cache, stream_id,
  *                                seq_len, ...)  with the step's plan, query

@@ -14,8 +14,12 @@
 // rotated key and the value written to the stream's new cache slot, the
 // rotated query to the workspace for the attention kernels that follow.
 // The angles are formed in double precision (a position of 10^5 times a
-// frequency near 1 leaves fp32 with ~10^-2 rad of error); the rotation
-// itself is fp32 and rounds once to the element type.
+// frequency near 1 leaves fp32 with ~10^-2 rad of error) and reduced modulo
+// 2*pi there; the sine and cosine of the reduced angle (|r| <= pi, rounded
+// to fp32: about 2^-22 rad off) are fp32, as is the rotation, which rounds
+// once to the element type.  A double sincos of the unreduced angle takes
+// the slow large-argument path on every new token past the first few
+// thousand positions.
 #include <math.h>
 
 #include "pp_internal.h"
@@ -66,52 +70,70 @@ __global__ __launch_bounds__(kAppendThreads) void append_rope_kernel(
     T* __restrict__ v_cache, int Hq, int Hkv, double rope_base, const int32_t* __restrict__ plan,
     const int32_t* __restrict__ counts, int64_t max_len, T* __restrict__ q_rot) {
   constexpr int HALF = D / 2;
-  constexpr int C4 = HALF / 4;  // chunks of 4 pairs per head
+  constexpr int C4 = HALF / 4;                 // items of 4 pairs per row
+  constexpr int VE = 16 / (int)sizeof(T);      // elements per 16-byte vector
   __shared__ float cs[HALF], sn[HALF];
   const int s = blockIdx.x, P = gridDim.x, tid = threadIdx.x;
+  // rotation items: the Hq query rows of the stream, then its Hkv key rows
+  const int nq = Hq * C4, nr = (Hq + Hkv) * C4, nv = Hkv * D / VE;
+  const int64_t qoff = (int64_t)s * Hq * D, knoff = (int64_t)s * Hkv * D;
+  auto row_off = [&](int it) -> int64_t {  // offset of item it within its rows
+    const int r = it < nq ? it : it - nq;
+    return (int64_t)(r / C4) * D + (r % C4) * 4;
+  };
+  auto src = [&](int it) -> const T* { return (it < nq ? q + qoff : k_new + knoff) + row_off(it); };
+  // Only the destination slot and the angle depend on the plan: the first
+  // item's inputs are loaded together with it, so one memory round trip
+  // precedes the rotation instead of three.
+  float a[4], b4[4];
+  u32x4 vv = {0, 0, 0, 0};
+  if (tid < nr) {
+    load4<T>(src(tid), a);
+    load4<T>(src(tid) + HALF, b4);
+  }
+  if (tid < nv) vv = *reinterpret_cast<const u32x4*>(v_new + knoff + (int64_t)tid * VE);
+  const int32_t doc_len = plan[0], count = counts[s];
   const int64_t seq_len = __builtin_amdgcn_readfirstlane(plan[1]);
-  if (seq_len < P || seq_len > max_len) return;
-  const int64_t slot = seq_len - P + s;
+  if (seq_len < P || seq_len > max_len) return;  // (uniform over the workgroup)
+  const int64_t slot = seq_len - P + s, koff = slot * Hkv * D;
   const bool rot = rope_base > 0.0;
   if (rot) {
     if (tid < HALF) {
-      const int64_t pos = (int64_t)plan[0] + counts[s] - 1;
+      const int64_t pos = (int64_t)doc_len + count - 1;
       const double theta = exp2(-(2.0 * tid / D) * log2(rope_base));
-      double sv, cv;
-      sincos((double)pos * theta, &sv, &cv);
-      cs[tid] = (float)cv;
-      sn[tid] = (float)sv;
+      const double x = (double)pos * theta;
+      constexpr double kTwoPi = 6.283185307179586476925286766559;
+      const float r = (float)fma(-rint(x * (1.0 / kTwoPi)), kTwoPi, x);
+      float sv, cv;
+      sincosf(r, &sv, &cv);
+      cs[tid] = cv;
+      sn[tid] = sv;
     }
     __syncthreads();
   }
-  // rows [0, nh) of D elements from src, each pair (i, i + D/2) rotated, to dst
-  auto rotate = [&](const T* src, T* dst, int nh) {
-    for (int it = tid; it < nh * C4; it += kAppendThreads) {
-      const int h = it / C4, i0 = (it % C4) * 4;
-      const int64_t lo = (int64_t)h * D + i0, hi = lo + HALF;
-      float a[4], b4[4];
-      load4<T>(src + lo, a);
-      load4<T>(src + hi, b4);
-      if (rot) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float c = cs[i0 + e], sv = sn[i0 + e];
-          const float x = a[e], y = b4[e];
-          a[e] = fmaf(x, c, -y * sv);
-          b4[e] = fmaf(y, c, x * sv);
-        }
-      }
-      store4<T>(dst + lo, a);
-      store4<T>(dst + hi, b4);
+  for (int it = tid; it < nr; it += kAppendThreads) {
+    if (it != tid) {
+      load4<T>(src(it), a);
+      load4<T>(src(it) + HALF, b4);
     }
-  };
-  const int64_t qoff = (int64_t)s * Hq * D, knoff = (int64_t)s * Hkv * D, koff = slot * Hkv * D;
-  rotate(q + qoff, q_rot + qoff, Hq);
-  rotate(k_new + knoff, k_cache + koff, Hkv);
-  constexpr int VE = 16 / (int)sizeof(T);  // elements per 16-byte vector
-  for (int it = tid; it < Hkv * D / VE; it += kAppendThreads)
-    *reinterpret_cast<u32x4*>(v_cache + koff + (int64_t)it * VE) =
-        *reinterpret_cast<const u32x4*>(v_new + knoff + (int64_t)it * VE);
+    const int i0 = (it % C4) * 4;
+    if (rot) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float c = cs[i0 + e], sv = sn[i0 + e];
+        const float x = a[e], y = b4[e];
+        a[e] = fmaf(x, c, -y * sv);
+        b4[e] = fmaf(y, c, x * sv);
+      }
+    }
+    T* dst = (it < nq ? q_rot + qoff : k_cache + koff) + row_off(it);
+    store4<T>(dst, a);
+    store4<T>(dst + HALF, b4);
+  }
+  for (int it = tid; it < nv; it += kAppendThreads) {
+    if (it != tid) vv = *reinterpret_cast<const u32x4*>(v_new + knoff + (int64_t)it * VE);
+    *reinterpret_cast<u32x4*>(v_cache + koff + (int64_t)it * VE) = vv;
+  }
 }
 
 }  // namespace
