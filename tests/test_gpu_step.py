@@ -332,6 +332,44 @@ def test_decode_append_grouped_heads(Hq, Hkv, D, dtype, rope_base):
         np.testing.assert_allclose(got, want, rtol=2e-6, atol=2e-6)
 
 
+def test_full_size_grouped_appending_step_sampled():
+    # the 12000-token document with 256 streams at its last answer step, 28
+    # query heads sharing 4 key/value heads (the grouped decode loop's shape)
+    doc, P, steps, H, Hkv, D, seed = 12000, 256, 32, 28, 4, 128, 1011
+    ids_full, _, base0 = decode_loop_layout(doc, P, steps, seed)
+    cap = len(ids_full)
+    t = steps - 1
+    b = base0 + t * P
+    k = torch.empty(cap, Hkv, D, dtype=torch.bfloat16)
+    v = torch.empty_like(k)
+    inp0 = decode_loop_step_inputs(H, D, P, cap, 3, 0, seed, base_len=base0, Hkv=Hkv)
+    k[:base0], v[:base0] = inp0["k0"], inp0["v0"]
+    for u in range(t):  # earlier answers, as already-rotated cache rows
+        inp = decode_loop_step_inputs(H, D, P, cap, 3, u, seed, base_len=base0, Hkv=Hkv)
+        k[base0 + u * P: base0 + (u + 1) * P] = inp["k_new"]
+        v[base0 + u * P: base0 + (u + 1) * P] = inp["v_new"]
+    ids = ids_full.copy()
+    ids[b:] = 0
+    step_inp = decode_loop_step_inputs(H, D, P, cap, 3, t, seed, Hkv=Hkv)
+    sid = _i32(ids)
+    kg, vg = k.to(DEV), v.to(DEV)
+    say(f"  gpu: full-size grouped appending step T={b + P} P={P} Hq={H} Hkv={Hkv}")
+    plan = pp.pp_step_plan(sid, _i32([b]), P, max_seq_len=cap)
+    out = pp.pp_attn_decode_append(step_inp["q"].to(DEV), step_inp["k_new"].to(DEV), step_inp["v_new"].to(DEV), kg,
+                                   vg, sid, plan, rope_base=1e6)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    streams = sorted({0, P - 1} | set(rng.choice(P, 6, replace=False).tolist()))
+    r = oracle_append_step(step_inp["q"], step_inp["k_new"], step_inp["v_new"], k, v, ids, b, 1.0 / np.sqrt(D), 1e6,
+                           streams=streams)
+    assert_close(out, r["out"], streams, what="full-size grouped appending step")
+    got = kg[b:b + P].double().cpu().numpy()
+    diff = np.abs(got - r["k_rot"])
+    assert (diff <= _rot_bound(r["k_rot"], step_inp["k_new"].double().numpy())).all()
+    np.testing.assert_array_equal(vg[b:b + P].view(torch.int16).cpu().numpy(),
+                                  step_inp["v_new"].view(torch.int16).numpy())
+
+
 def test_graph_of_the_grouped_step_replays_every_step():
     # 28 query heads sharing 4 key/value heads: one capture of (plan + 2
     # layers + advance), replayed 12 times, against the oracle's own loop
