@@ -513,6 +513,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-decode-loop", action="store_true",
                     help="skip the 32-step x 32-layer appending loop (eager and graph-replayed)")
+    ap.add_argument("--decode-loop-heads", choices=("both", "mha", "grouped"), default="both",
+                    help="which appending loops to run: 32 heads, 28 query heads on 4 key/value heads, or both")
     ap.add_argument("--no-answer-sweep", action="store_true",
                     help="skip the long-answer sweep (8k document, 128 streams, 128-1024 answer tokens)")
     ap.add_argument("--no-prefill", action="store_true",
@@ -651,12 +653,15 @@ def main():
     loop = None
     if not args.no_decode_loop:
         log("bench: 32-step x 32-layer appending loop")
-        loop = decode_loop(torch, pp, dev, with_oracle=not args.no_cpu_baseline)
-        torch.cuda.empty_cache()
-        log("bench: appending loop, 28 query heads sharing 4 key/value heads")
-        loop["grouped_heads"] = decode_loop(torch, pp, dev, layers=28, H=28, Hkv=4, with_oracle=False,
-                                            model="qwen7b_shape")
-        torch.cuda.empty_cache()
+        loop = {}
+        if args.decode_loop_heads != "grouped":
+            loop = decode_loop(torch, pp, dev, with_oracle=not args.no_cpu_baseline)
+            torch.cuda.empty_cache()
+        if args.decode_loop_heads != "mha":
+            log("bench: appending loop, 28 query heads sharing 4 key/value heads")
+            loop["grouped_heads"] = decode_loop(torch, pp, dev, layers=28, H=28, Hkv=4, with_oracle=False,
+                                                model="qwen7b_shape")
+            torch.cuda.empty_cache()
 
     sweep = None
     if not args.no_answer_sweep:
