@@ -255,6 +255,41 @@ pp_status_t pp_attn_decode_append(const void* q, const void* k_new, const void* 
                                   pp_dtype_t dtype, void* workspace, size_t workspace_bytes,
                                   void* hip_stream);
 
+/* The appending step for B requests at once (request slots of a server:
+ * Parallel Prompting project page, "Continuous batching", where a finished
+ * request's slot takes the next one).  Request b is what pp_step_plan and
+ * pp_attn_decode_append do for one request, on its own rows:
+ *   stream_id        device int32[B][max_seq_len]
+ *   base_len         device int32[B]: request b's step starts at
+ *                    base_len[b]; a value outside [0, max_seq_len - P]
+ *                    marks an idle slot (empty plan, no id, cache row or
+ *                    output written by the layers except zeros in out)
+ *   active           device int32[B][P] or NULL: 0 retires stream s of
+ *                    request b (it lists nothing and its output is zero;
+ *                    its new slot gets its id, but no key or value is
+ *                    written there: no stream sees that slot)
+ *   plan_head        device int32[2 * B], written: doc_len of requests
+ *                    0..B-1, then their seq_len (for B = 1 the layout of
+ *                    pp_step_plan)
+ *   plan_counts      device int32[B][P];  plan_slots int32[B][P][plan_capacity]
+ *   q, out           [B][P][Hq][d];  k_new, v_new [B][P][Hkv][d]
+ *   k_cache, v_cache [B][max_seq_len][Hkv][d]
+ * Workspace: pp_attn_multi_workspace_bytes(max_seq_len, B, P, Hq, Hkv, d,
+ * dtype).  Buffers are caller-owned device memory; the overlap rules and
+ * errors are those of the one-request calls, with PP_ERR_INVALID_ARG also for
+ * B out of [1, PP_MAX_REQUESTS]. */
+pp_status_t pp_step_plan_multi(int32_t* stream_id, const int32_t* base_len, const int32_t* active,
+                               int64_t max_seq_len, int32_t B, int32_t P, int32_t* plan_head,
+                               int32_t* plan_counts, int32_t* plan_slots, int64_t plan_capacity,
+                               void* hip_stream);
+pp_status_t pp_attn_decode_append_multi(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                                        void* v_cache, const int32_t* stream_id, const int32_t* active,
+                                        int64_t max_seq_len, int32_t B, int32_t P, int32_t Hq, int32_t Hkv,
+                                        int32_t d, float scale, double rope_base, const int32_t* plan_head,
+                                        const int32_t* plan_counts, const int32_t* plan_slots,
+                                        int64_t plan_capacity, void* out, pp_dtype_t dtype, void* workspace,
+                                        size_t workspace_bytes, void* hip_stream);
+
 /* Prefill of the whole packed request -- the document and every stream's
  * question tokens as one sequence, attended once (Parallel Prompting project
  * page, "How it works" and its illustration: the document and all questions

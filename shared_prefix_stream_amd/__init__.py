@@ -42,6 +42,8 @@ __all__ = [
     "PROFILE_STAGES",
     "pp_attn_decode_planned",
     "pp_step_plan",
+    "pp_step_plan_multi",
+    "pp_attn_decode_append_multi",
     "pp_attn_decode_append",
     "prefill_workspace_bytes",
     "pp_attn_prefill",
@@ -113,6 +115,11 @@ def _load():
     lib.pp_attn_decode_append.restype = ctypes.c_int
     lib.pp_attn_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, f32, ctypes.c_double, vp,
                                           vp, vp, i64, vp, ctypes.c_int, vp, sz, vp]
+    lib.pp_step_plan_multi.restype = ctypes.c_int
+    lib.pp_step_plan_multi.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp, vp, i64, vp]
+    lib.pp_attn_decode_append_multi.restype = ctypes.c_int
+    lib.pp_attn_decode_append_multi.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, f32,
+                                                ctypes.c_double, vp, vp, vp, i64, vp, ctypes.c_int, vp, sz, vp]
     lib.pp_attn_prefill_workspace_bytes.restype = sz
     lib.pp_attn_prefill_workspace_bytes.argtypes = [i64, i32, i32, ctypes.c_int]
     lib.pp_attn_prefill.restype = ctypes.c_int
@@ -395,6 +402,104 @@ def pp_attn_decode_append(q, k_new, v_new, k_cache, v_cache, stream_id, plan, sc
         slots.data_ptr() if cap > 0 else None, cap, out.data_ptr(), code, workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _stream_handle(q.device))
     _check(st)
+    return out
+
+
+def pp_step_plan_multi(stream_id, base_len, P: int, active=None, tail_capacity: Optional[int] = None, plan=None):
+    """Start an appending step for B request slots: stream_id [B, T] and
+    base_len [B] (request b's new slots at base_len[b] + s; a value outside
+    [0, T - P] idles the slot), optional active [B, P] (0 retires a stream),
+    all int32 on the GPU.  Returns the plan (head [2B] = doc lengths then
+    step lengths, counts [B, P], slots [B, P, capacity]), written into `plan`
+    when given."""
+    import torch
+
+    _gpu_int32("stream_id", stream_id)
+    _gpu_int32("base_len", base_len)
+    if stream_id.dim() != 2 or base_len.shape != (stream_id.shape[0],):
+        raise ValueError("stream_id must be [B, T] and base_len [B]")
+    B, T = stream_id.shape
+    if active is not None:
+        _gpu_int32("active", active)
+        if tuple(active.shape) != (B, P):
+            raise ValueError(f"active must be [B, P] = {(B, P)}")
+    dev = stream_id.device
+    if plan is None:
+        if tail_capacity is None:
+            tail_capacity = (min(int(T), 2048) + 3) // 4 * 4
+        head = torch.zeros(2 * B, dtype=torch.int32, device=dev)
+        counts = torch.zeros(B, P, dtype=torch.int32, device=dev)
+        slots = torch.full((B, P, max(tail_capacity, 1)), -1, dtype=torch.int32, device=dev)[:, :, :tail_capacity]
+    else:
+        head, counts, slots = plan
+        for name, t in (("head", head), ("counts", counts)):
+            _gpu_int32(f"plan {name}", t)
+        if head.numel() < 2 * B or tuple(counts.shape) != (B, P) or slots.dim() != 3 or slots.shape[:2] != (B, P):
+            raise ValueError("plan must be (head [2B], counts [B, P], slots [B, P, capacity])")
+    tail_capacity = int(slots.shape[2])
+    if tail_capacity > 0:
+        _gpu_int32("plan slots", slots)
+    _check(_load().pp_step_plan_multi(stream_id.data_ptr(), base_len.data_ptr(),
+                                      None if active is None else active.data_ptr(), int(T), int(B), int(P),
+                                      head.data_ptr(), counts.data_ptr(),
+                                      slots.data_ptr() if tail_capacity > 0 else None, tail_capacity,
+                                      _stream_handle(dev)))
+    return head, counts, slots
+
+
+def pp_attn_decode_append_multi(q, k_new, v_new, k_cache, v_cache, stream_id, plan, active=None,
+                                scale: Optional[float] = None, rope_base: float = 10000.0, out=None, workspace=None):
+    """One layer of an appending step of B request slots started by
+    pp_step_plan_multi: q [B, P, Hq, d], k_new, v_new [B, P, Hkv, d],
+    k_cache, v_cache [B, T, Hkv, d], stream_id [B, T], optional active
+    [B, P].  Returns out [B, P, Hq, d] (zeros for idle slots and retired
+    streams) without synchronising."""
+    import torch
+
+    for name, t in (("q", q), ("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache), ("v_cache", v_cache),
+                    ("stream_id", stream_id)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if q.dim() != 4 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("q must be [B, P, Hq, d] and k_cache, v_cache [B, T, Hkv, d]")
+    B, P, H, d = q.shape
+    _, T, Hkv, dk = k_cache.shape
+    if k_cache.shape[0] != B or dk != d:
+        raise ValueError(f"k_cache {tuple(k_cache.shape)} does not match q {tuple(q.shape)}")
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if tuple(t.shape) != (B, P, Hkv, d):
+            raise ValueError(f"{name} must be [B, P, Hkv, d] = {(B, P, Hkv, d)}")
+    if not (q.dtype == k_new.dtype == v_new.dtype == k_cache.dtype == v_cache.dtype):
+        raise ValueError("q, k_new, v_new, k_cache and v_cache must share one dtype")
+    if stream_id.dtype != torch.int32 or tuple(stream_id.shape) != (B, T):
+        raise ValueError("stream_id must be an int32 [B, T] tensor")
+    if active is not None:
+        _gpu_int32("active", active)
+        if tuple(active.shape) != (B, P) or not active.is_contiguous():
+            raise ValueError(f"active must be a contiguous [B, P] = {(B, P)} tensor")
+    head, counts, slots = plan
+    for name, t in (("head", head), ("counts", counts), ("slots", slots)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.int32:
+            raise ValueError(f"plan {name} must be an int32 GPU tensor")
+    if head.numel() < 2 * B or tuple(counts.shape) != (B, P) or slots.dim() != 3 or slots.shape[:2] != (B, P):
+        raise ValueError("plan must be (head [2B], counts [B, P], slots [B, P, capacity]) from pp_step_plan_multi")
+    cap = int(slots.shape[2])
+    if cap > 0 and not slots.is_contiguous():
+        raise ValueError("plan slots must be contiguous")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    code = _dtype_code(q.dtype)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_cuda or not out.is_contiguous():
+        raise ValueError("out must be a contiguous GPU tensor shaped and typed like q")
+    if workspace is None:
+        workspace = torch.empty(multi_workspace_bytes(T, B, P, H, Hkv, d, code), dtype=torch.uint8, device=q.device)
+    _check(_load().pp_attn_decode_append_multi(
+        q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        stream_id.data_ptr(), None if active is None else active.data_ptr(), int(T), int(B), int(P), int(H),
+        int(Hkv), int(d), scale, float(rope_base), head.data_ptr(), counts.data_ptr(),
+        slots.data_ptr() if cap > 0 else None, cap, out.data_ptr(), code, workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream_handle(q.device)))
     return out
 
 

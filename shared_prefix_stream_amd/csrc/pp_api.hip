@@ -135,32 +135,31 @@ pp_status_t decode_impl(Path path, const void* q, const void* k, const void* v, 
   if (overlaps(workspace, workspace_bytes, q, nq) || overlaps(workspace, workspace_bytes, k, nkv) ||
       overlaps(workspace, workspace_bytes, v, nkv) || overlaps(workspace, workspace_bytes, sid, nid))
     return fail(PP_ERR_INVALID_ARG, "workspace overlaps an input");
+  // a caller's plan: head (doc_len per request, then with an append their
+  // seq_len), counts [B][P], slots [B][P][capacity]
+  const size_t nh = (size_t)(ap ? 2 : 1) * B * 4, nc = (size_t)B * P * 4,
+               ns = xp ? (size_t)B * P * (size_t)(xp->capacity > 0 ? xp->capacity : 0) * 4 : 0;
   if (xp) {
     if (!xp->doc_len || !xp->counts) return fail(PP_ERR_INVALID_ARG, "null plan_doc_len or plan_counts");
     if (xp->capacity < 0 || (xp->capacity > 0 && !xp->slots))
       return fail(PP_ERR_INVALID_ARG, "plan_slots is null or plan_capacity negative");
-    const size_t ns = (size_t)P * (size_t)xp->capacity * 4;
-    if (overlaps(out, nq, xp->doc_len, 4) || overlaps(out, nq, xp->counts, (size_t)P * 4) ||
-        overlaps(out, nq, xp->slots, ns) || overlaps(workspace, workspace_bytes, xp->doc_len, 4) ||
-        overlaps(workspace, workspace_bytes, xp->counts, (size_t)P * 4) ||
+    if (overlaps(out, nq, xp->doc_len, nh) || overlaps(out, nq, xp->counts, nc) || overlaps(out, nq, xp->slots, ns) ||
+        overlaps(workspace, workspace_bytes, xp->doc_len, nh) || overlaps(workspace, workspace_bytes, xp->counts, nc) ||
         overlaps(workspace, workspace_bytes, xp->slots, ns))
       return fail(PP_ERR_INVALID_ARG, "a plan buffer overlaps out or the workspace");
   }
-  if (ap) {  // (always with a caller's plan: {doc_len, seq_len}, counts, slots)
-    if (overlaps(out, nq, xp->doc_len, 8) || overlaps(workspace, workspace_bytes, xp->doc_len, 8))
-      return fail(PP_ERR_INVALID_ARG, "a plan buffer overlaps out or the workspace");
+  if (ap) {  // (always with a caller's plan)
     if (P > seq_len) return fail(PP_ERR_INVALID_ARG, "P=%d exceeds max_seq_len=%lld", P, (long long)seq_len);
     if (!ap->k_new || !ap->v_new) return fail(PP_ERR_INVALID_ARG, "null k_new or v_new");
     if (!aligned16(ap->k_new) || !aligned16(ap->v_new))
       return fail(PP_ERR_INVALID_ARG, "k_new and v_new must be 16-byte aligned");
     if (!isfinite(ap->rope_base)) return fail(PP_ERR_INVALID_ARG, "rope_base is not finite");
     // the caches are written: nothing read in the step may share their bytes
-    const size_t nn = (size_t)P * Hkv * d * es;  // new keys (values) of the step
+    const size_t nn = (size_t)B * P * Hkv * d * es;  // new keys (values) of the step
     for (const void* w : {k, v})
       if (overlaps(w, nkv, q, nq) || overlaps(w, nkv, ap->k_new, nn) || overlaps(w, nkv, ap->v_new, nn) ||
           overlaps(w, nkv, sid, nid) || overlaps(w, nkv, workspace, workspace_bytes) ||
-          overlaps(w, nkv, xp->doc_len, 8) || overlaps(w, nkv, xp->counts, (size_t)P * 4) ||
-          overlaps(w, nkv, xp->slots, (size_t)P * (size_t)(xp->capacity > 0 ? xp->capacity : 0) * 4))
+          overlaps(w, nkv, xp->doc_len, nh) || overlaps(w, nkv, xp->counts, nc) || overlaps(w, nkv, xp->slots, ns))
         return fail(PP_ERR_INVALID_ARG, "k_cache or v_cache overlaps another argument");
     if (overlaps(k, nkv, v, nkv)) return fail(PP_ERR_INVALID_ARG, "k_cache and v_cache overlap");
     if (overlaps(out, nq, ap->k_new, nn) || overlaps(out, nq, ap->v_new, nn) ||
@@ -186,7 +185,7 @@ pp_status_t decode_impl(Path path, const void* q, const void* k, const void* v, 
     ws.slots = const_cast<int32_t*>(xp->slots);
     ws.cap = xp->capacity;
   }
-  if (ap) ws.dyn_len = xp->doc_len + 1;  // {doc_len, seq_len} of the step
+  if (ap && !bt.seq_lens) ws.dyn_len = xp->doc_len + 1;  // {doc_len, seq_len} of the step
 
   // optional profiling events around the launches
   auto mark = [&](int i) -> hipError_t {
@@ -196,7 +195,8 @@ pp_status_t decode_impl(Path path, const void* q, const void* k, const void* v, 
   if (e == hipSuccess && !xp) e = pp::launch_plan(sid, seq_len, P, ws.plan, ws.counts, ws.slots, ws.cap, stream, bt);
   if (e == hipSuccess && ap) {  // new keys and values into the caches, rotated queries into the workspace
     e = pp::launch_append_rope(q, ap->k_new, ap->v_new, const_cast<void*>(k), const_cast<void*>(v), P, H, Hkv, d, dtype,
-                               ap->rope_base, ws.plan, ws.counts, seq_len, ws.q_rot, stream);
+                               ap->rope_base, ws.plan, ws.counts, seq_len, ws.q_rot, stream, B, bt.kv_stride,
+                               bt.active);
     q = ws.q_rot;
   }
   if (e == hipSuccess) e = mark(1);
@@ -294,9 +294,10 @@ pp_status_t pp_attn_decode_planned(const void* q, const void* k_cache, const voi
                      workspace_bytes, hip_stream, nullptr, &xp);
 }
 
-pp_status_t pp_step_plan(int32_t* stream_id, const int32_t* base_len, int64_t max_seq_len, int32_t P,
-                         int32_t* plan_head, int32_t* plan_counts, int32_t* plan_slots, int64_t plan_capacity,
-                         void* hip_stream) {
+pp_status_t pp_step_plan_multi(int32_t* stream_id, const int32_t* base_len, const int32_t* active,
+                               int64_t max_seq_len, int32_t B, int32_t P, int32_t* plan_head, int32_t* plan_counts,
+                               int32_t* plan_slots, int64_t plan_capacity, void* hip_stream) {
+  if (B < 1 || B > PP_MAX_REQUESTS) return fail(PP_ERR_INVALID_ARG, "B=%d out of range [1, %d]", B, PP_MAX_REQUESTS);
   if (max_seq_len < 1 || max_seq_len > PP_MAX_SEQ_LEN)
     return fail(PP_ERR_INVALID_ARG, "max_seq_len=%lld out of range", (long long)max_seq_len);
   if (P < 1 || P > PP_MAX_STREAMS || P > max_seq_len)
@@ -305,20 +306,34 @@ pp_status_t pp_step_plan(int32_t* stream_id, const int32_t* base_len, int64_t ma
   if (plan_capacity < 0 || (plan_capacity > 0 && !plan_slots))
     return fail(PP_ERR_INVALID_ARG, "plan_slots is null or plan_capacity negative");
   if (!aligned16(stream_id)) return fail(PP_ERR_INVALID_ARG, "stream_id must be 16-byte aligned");
-  const size_t nid = (size_t)max_seq_len * 4, nc = (size_t)P * 4, ns = (size_t)P * (size_t)plan_capacity * 4;
+  const size_t nid = (size_t)B * max_seq_len * 4, nc = (size_t)B * P * 4,
+               ns = (size_t)B * P * (size_t)plan_capacity * 4, nb = (size_t)B * 4, na = active ? nc : 0;
   const void* outs[3] = {plan_head, plan_counts, plan_slots};
-  const size_t nout[3] = {8, nc, ns};
+  const size_t nout[3] = {2 * nb, nc, ns};
   for (int i = 0; i < 3; ++i) {
-    if (overlaps(outs[i], nout[i], stream_id, nid) || overlaps(outs[i], nout[i], base_len, 4))
-      return fail(PP_ERR_INVALID_ARG, "a plan buffer overlaps stream_id or base_len");
+    if (overlaps(outs[i], nout[i], stream_id, nid) || overlaps(outs[i], nout[i], base_len, nb) ||
+        overlaps(outs[i], nout[i], active, na))
+      return fail(PP_ERR_INVALID_ARG, "a plan buffer overlaps stream_id, base_len or active");
     for (int j = i + 1; j < 3; ++j)
       if (overlaps(outs[i], nout[i], outs[j], nout[j])) return fail(PP_ERR_INVALID_ARG, "plan buffers overlap");
   }
-  if (overlaps(base_len, 4, stream_id, nid)) return fail(PP_ERR_INVALID_ARG, "base_len overlaps stream_id");
+  if (overlaps(base_len, nb, stream_id, nid) || overlaps(active, na, stream_id, nid))
+    return fail(PP_ERR_INVALID_ARG, "base_len or active overlaps stream_id");
+  pp::Batch bt;
+  bt.B = B;
+  bt.id_stride = max_seq_len;
+  bt.active = active;
   hipError_t e = pp::launch_plan_append(stream_id, base_len, max_seq_len, P, plan_head, plan_counts, plan_slots,
-                                        plan_capacity, static_cast<hipStream_t>(hip_stream));
+                                        plan_capacity, static_cast<hipStream_t>(hip_stream), bt);
   if (e != hipSuccess) return fail(PP_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+pp_status_t pp_step_plan(int32_t* stream_id, const int32_t* base_len, int64_t max_seq_len, int32_t P,
+                         int32_t* plan_head, int32_t* plan_counts, int32_t* plan_slots, int64_t plan_capacity,
+                         void* hip_stream) {
+  return pp_step_plan_multi(stream_id, base_len, nullptr, max_seq_len, 1, P, plan_head, plan_counts, plan_slots,
+                            plan_capacity, hip_stream);
 }
 
 pp_status_t pp_attn_decode_append(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
@@ -332,6 +347,27 @@ pp_status_t pp_attn_decode_append(const void* q, const void* k_new, const void* 
   const AppendArgs ap{k_new, v_new, rope_base};
   pp::Batch bt;
   bt.G = Hq / Hkv;
+  return decode_impl(Path::kParallel, q, k_cache, v_cache, stream_id, max_seq_len, P, Hq, d, scale, out, dtype,
+                     workspace, workspace_bytes, hip_stream, nullptr, &xp, &ap, bt);
+}
+
+pp_status_t pp_attn_decode_append_multi(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                                        void* v_cache, const int32_t* stream_id, const int32_t* active,
+                                        int64_t max_seq_len, int32_t B, int32_t P, int32_t Hq, int32_t Hkv, int32_t d,
+                                        float scale, double rope_base, const int32_t* plan_head,
+                                        const int32_t* plan_counts, const int32_t* plan_slots, int64_t plan_capacity,
+                                        void* out, pp_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                        void* hip_stream) {
+  if (B < 1 || B > PP_MAX_REQUESTS) return fail(PP_ERR_INVALID_ARG, "B=%d out of range [1, %d]", B, PP_MAX_REQUESTS);
+  if (Hkv < 1 || Hq % Hkv != 0) return fail(PP_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (!plan_head) return fail(PP_ERR_INVALID_ARG, "null plan_head");
+  const ExternalPlan xp{plan_head, plan_counts, plan_slots, plan_capacity};
+  const AppendArgs ap{k_new, v_new, rope_base};
+  pp::Batch bt;
+  bt.B = B;
+  bt.G = Hq / Hkv;
+  bt.seq_lens = plan_head + B;  // each request's step length, from the step's plan
+  bt.active = active;
   return decode_impl(Path::kParallel, q, k_cache, v_cache, stream_id, max_seq_len, P, Hq, d, scale, out, dtype,
                      workspace, workspace_bytes, hip_stream, nullptr, &xp, &ap, bt);
 }

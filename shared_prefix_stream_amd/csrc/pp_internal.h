@@ -302,7 +302,8 @@ hipError_t launch_plan(const int32_t* sid, int64_t seq_len, int P, int32_t* plan
 // plan[1] = seq_len.  max_len bounds seq_len; a base past it gives an empty
 // plan.
 hipError_t launch_plan_append(int32_t* sid, const int32_t* base_len, int64_t max_len, int P, int32_t* plan,
-                              int32_t* counts, int32_t* slots, int64_t cap, hipStream_t stream);
+                              int32_t* counts, int32_t* slots, int64_t cap, hipStream_t stream,
+                              const Batch& bt = Batch());
 
 // Rotary embedding of the step's new queries and keys at their shared
 // positions (from the plan), and the new keys and values written to the
@@ -310,7 +311,8 @@ hipError_t launch_plan_append(int32_t* sid, const int32_t* base_len, int64_t max
 // rope_base <= 0: no rotation.
 hipError_t launch_append_rope(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                               int P, int Hq, int Hkv, int d, pp_dtype_t dtype, double rope_base, const int32_t* plan,
-                              const int32_t* counts, int64_t max_len, void* q_rot, hipStream_t stream);
+                              const int32_t* counts, int64_t max_len, void* q_rot, hipStream_t stream, int B = 1,
+                              int64_t kv_stride = 0, const int32_t* active = nullptr);
 
 // Document part, all P queries of a head at once: split-K partial softmax
 // states over [0, doc_len).  Returns the number of splits it will use via

@@ -31,13 +31,14 @@ constexpr int64_t kPlanChunk = kPlanWaveSpan * kPlanNW;          // 32K slots pe
 //      are counted only).
 // One global round trip per 32K slots; no atomics decide positions.
 //
-// APPEND (a decode step that appends one slot per stream): the step starts
-// at base = *base_len, stream s's new slot is base + s, and the plan covers
-// seq_len = base + P, where the `seq_len` argument is only the largest
-// allowed length.  The ids of [base, base + P) are taken as s + 1 whatever
-// memory holds (other workgroups may be writing them), workgroup s stores
-// its own, and plan[1] = seq_len.  A base outside [0, limit - P] gives an
-// empty plan (plan[0] = plan[1] = 0, no counts, nothing written).
+// APPEND (a decode step that appends one slot per stream): request b's
+// step starts at base = base_len[b], stream s's new slot is base + s, and
+// the plan covers seq_len = base + P, where the `seq_len` argument is only
+// the largest allowed length.  The ids of [base, base + P) are taken as
+// s + 1 whatever memory holds (other workgroups may be writing them),
+// workgroup (s, b) stores its own, and plan[B + b] = seq_len (plan[1] for
+// one request).  A base outside [0, limit - P] gives an empty plan
+// (plan[b] = plan[B + b] = 0, no counts, nothing written): an idle request.
 //
 // Several requests (grid.y = B, single-request layout otherwise): workgroup
 // (s, b) plans stream s of request b over that request's ids and length;
@@ -55,18 +56,20 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
   const int s = blockIdx.x;                     // stream within the request
   const int sl = b * (int)gridDim.x + s;        // stream of the launch
   sid += b * bt.id_stride;
+  if constexpr (APPEND) sid_out += b * bt.id_stride;
   if constexpr (!APPEND) seq_len = request_len(bt, b, seq_len);
   const unsigned live = stream_active(bt, sl) ? 1u : 0u;  // a retired stream lists nothing
   const int s1 = s + 1;
   const uint64_t below = (1ull << lane) - 1ull;  // lanes before this one
   int64_t app = seq_len;  // first appended slot
   if constexpr (APPEND) {
-    const int64_t bb = __builtin_amdgcn_readfirstlane(base_len[0]);
+    // head: doc_len of the B requests, then their seq_len
+    const int64_t bb = __builtin_amdgcn_readfirstlane(base_len[b]);
     const int64_t P = gridDim.x;
-    if (bb < 0 || bb > seq_len - P) {
+    if (bb < 0 || bb > seq_len - P) {  // an idle request: empty plan, no ids
       if (tid == 0) {
-        counts[s] = 0;
-        if (s == 0) plan[0] = plan[1] = 0;
+        counts[sl] = 0;
+        if (s == 0) plan[b] = plan[gridDim.y + b] = 0;
       }
       return;
     }
@@ -176,7 +179,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     if (s == 0) plan[b] = (int32_t)(doc_len < 0 ? seq_len : doc_len);
     if constexpr (APPEND) {
       sid_out[app + s] = s1;
-      if (s == 0) plan[1] = (int32_t)seq_len;
+      if (s == 0) plan[gridDim.y + b] = (int32_t)seq_len;
     }
   }
 }
@@ -191,8 +194,9 @@ hipError_t launch_plan(const int32_t* sid, int64_t seq_len, int P, int32_t* plan
 }
 
 hipError_t launch_plan_append(int32_t* sid, const int32_t* base_len, int64_t max_len, int P, int32_t* plan,
-                              int32_t* counts, int32_t* slots, int64_t cap, hipStream_t stream) {
-  plan_kernel<true><<<P, kPlanThreads, 0, stream>>>(sid, max_len, plan, counts, slots, cap, sid, base_len, Batch());
+                              int32_t* counts, int32_t* slots, int64_t cap, hipStream_t stream, const Batch& bt) {
+  plan_kernel<true><<<dim3(P, bt.B), kPlanThreads, 0, stream>>>(sid, max_len, plan, counts, slots, cap, sid, base_len,
+                                                                bt);
   return hipGetLastError();
 }
 

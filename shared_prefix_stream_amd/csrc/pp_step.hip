@@ -59,24 +59,33 @@ __device__ __forceinline__ void store4<float>(float* p, const float* f) {
   *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
 }
 
-// plan = {doc_len, seq_len} of the step (from the appending plan kernel);
-// the step's new slots are [seq_len - P, seq_len).  An empty or out-of-range
-// plan writes nothing.  Hq query heads, Hkv key/value heads (Hq = Hkv
+// Workgroup (s, b): stream s of request b.  plan = {doc_len[B], seq_len[B]}
+// of the step (from the appending plan kernel); request b's new slots are
+// [seq_len[b] - P, seq_len[b]).  An empty or out-of-range plan writes
+// nothing (an idle request).  Hq query heads, Hkv key/value heads (Hq = Hkv
 // without grouping): the queries have Hq rows per stream, the new keys and
-// values Hkv.
+// values Hkv; request b's caches start kv_stride elements after request
+// b - 1's.  A retired stream (active[s] == 0) lists nothing, so it has no
+// position: its query is rotated (the attention discards it) but its key and
+// value are not written.
 template <typename T, int D>
 __global__ __launch_bounds__(kAppendThreads) void append_rope_kernel(
     const T* __restrict__ q, const T* __restrict__ k_new, const T* __restrict__ v_new, T* __restrict__ k_cache,
     T* __restrict__ v_cache, int Hq, int Hkv, double rope_base, const int32_t* __restrict__ plan,
-    const int32_t* __restrict__ counts, int64_t max_len, T* __restrict__ q_rot) {
+    const int32_t* __restrict__ counts, int64_t max_len, T* __restrict__ q_rot, int64_t kv_stride,
+    const int32_t* __restrict__ active) {
   constexpr int HALF = D / 2;
   constexpr int C4 = HALF / 4;                 // items of 4 pairs per row
   constexpr int VE = 16 / (int)sizeof(T);      // elements per 16-byte vector
   __shared__ float cs[HALF], sn[HALF];
-  const int s = blockIdx.x, P = gridDim.x, tid = threadIdx.x;
+  const int s = blockIdx.x, P = gridDim.x, b = blockIdx.y, B = gridDim.y, tid = threadIdx.x;
+  const int sl = b * P + s;  // stream of the launch
+  k_cache += b * kv_stride;
+  v_cache += b * kv_stride;
   // rotation items: the Hq query rows of the stream, then its Hkv key rows
-  const int nq = Hq * C4, nr = (Hq + Hkv) * C4, nv = Hkv * D / VE;
-  const int64_t qoff = (int64_t)s * Hq * D, knoff = (int64_t)s * Hkv * D;
+  const bool live = !active || active[sl] != 0;
+  const int nq = Hq * C4, nr = live ? (Hq + Hkv) * C4 : nq, nv = live ? Hkv * D / VE : 0;
+  const int64_t qoff = (int64_t)sl * Hq * D, knoff = (int64_t)sl * Hkv * D;
   auto row_off = [&](int it) -> int64_t {  // offset of item it within its rows
     const int r = it < nq ? it : it - nq;
     return (int64_t)(r / C4) * D + (r % C4) * 4;
@@ -92,8 +101,8 @@ __global__ __launch_bounds__(kAppendThreads) void append_rope_kernel(
     load4<T>(src(tid) + HALF, b4);
   }
   if (tid < nv) vv = *reinterpret_cast<const u32x4*>(v_new + knoff + (int64_t)tid * VE);
-  const int32_t doc_len = plan[0], count = counts[s];
-  const int64_t seq_len = __builtin_amdgcn_readfirstlane(plan[1]);
+  const int32_t doc_len = plan[b], count = counts[sl];
+  const int64_t seq_len = __builtin_amdgcn_readfirstlane(plan[B + b]);
   if (seq_len < P || seq_len > max_len) return;  // (uniform over the workgroup)
   const int64_t slot = seq_len - P + s, koff = slot * Hkv * D;
   const bool rot = rope_base > 0.0;
@@ -140,12 +149,13 @@ __global__ __launch_bounds__(kAppendThreads) void append_rope_kernel(
 
 hipError_t launch_append_rope(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                               int P, int Hq, int Hkv, int d, pp_dtype_t dtype, double rope_base, const int32_t* plan,
-                              const int32_t* counts, int64_t max_len, void* q_rot, hipStream_t stream) {
+                              const int32_t* counts, int64_t max_len, void* q_rot, hipStream_t stream, int B,
+                              int64_t kv_stride, const int32_t* active) {
 #define PP_APPEND_LAUNCH(TT, DD)                                                                              \
-  append_rope_kernel<TT, DD><<<P, kAppendThreads, 0, stream>>>(                                               \
+  append_rope_kernel<TT, DD><<<dim3(P, B), kAppendThreads, 0, stream>>>(                                      \
       static_cast<const TT*>(q), static_cast<const TT*>(k_new), static_cast<const TT*>(v_new),                \
       static_cast<TT*>(k_cache), static_cast<TT*>(v_cache), Hq, Hkv, rope_base, plan, counts, max_len,       \
-      static_cast<TT*>(q_rot))
+      static_cast<TT*>(q_rot), kv_stride, active)
   if (dtype == PP_BF16) {
     if (d == 128) PP_APPEND_LAUNCH(uint16_t, 128);
     else PP_APPEND_LAUNCH(uint16_t, 64);

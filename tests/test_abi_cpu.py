@@ -206,6 +206,48 @@ def test_decode_append_validation():
     assert lib.pp_last_error_message().decode() != ""
 
 
+def test_step_plan_multi_validation():
+    lib = pp.raw()
+    BASE, ACT, HEAD, CNT, SL = 0x60000000, 0x68000000, 0x70000000, 0x80000000, 0x90000000
+
+    def call(sid=SID, base=BASE, act=ACT, max_len=1000, B=3, P=8, head=HEAD, cnt=CNT, sl=SL, cap=16):
+        return lib.pp_step_plan_multi(sid, base, act, max_len, B, P, head, cnt, sl, cap, None)
+
+    assert call(B=0) == pp.PP_ERR_INVALID_ARG
+    assert call(B=70000) == pp.PP_ERR_INVALID_ARG
+    assert call(P=1001) == pp.PP_ERR_INVALID_ARG
+    assert call(base=None) == pp.PP_ERR_INVALID_ARG
+    assert call(sid=SID + 4) == pp.PP_ERR_INVALID_ARG                  # misaligned ids
+    assert call(head=SID + 3 * 1000 * 4 - 8) == pp.PP_ERR_INVALID_ARG  # head over request 2's ids
+    assert call(act=SID + 2 * 1000 * 4) == pp.PP_ERR_INVALID_ARG        # active inside the ids
+    assert call(head=ACT + 3 * 8 * 4 - 4) == pp.PP_ERR_INVALID_ARG      # head over the active flags
+    assert call(cnt=HEAD + 20) == pp.PP_ERR_INVALID_ARG                 # counts over the 2B-entry head
+    assert call(sl=CNT + 3 * 8 * 4 - 4) == pp.PP_ERR_INVALID_ARG        # lists over the B*P counts
+    assert lib.pp_last_error_message().decode() != ""
+
+
+def test_decode_append_multi_validation():
+    lib = pp.raw()
+    KN, VN, ACT, HEAD, CNT, SL = 0x70000000, 0x78000000, 0x7C000000, 0x80000000, 0x90000000, 0xA0000000
+    B, P, Hq, Hkv, T = 3, 8, 8, 2, 1000
+    ws_bytes = lib.pp_attn_multi_workspace_bytes(T, B, P, Hq, Hkv, 128, pp.PP_BF16)
+    assert ws_bytes > lib.pp_attn_multi_workspace_bytes(T, 1, P, Hq, Hkv, 128, pp.PP_BF16)
+
+    def call(q=Q, kn=KN, vn=VN, k=K, v=V, act=ACT, B=B, Hq=Hq, Hkv=Hkv, head=HEAD, out=OUT, ws=WS, wsb=ws_bytes):
+        return lib.pp_attn_decode_append_multi(q, kn, vn, k, v, SID, act, T, B, P, Hq, Hkv, 128, 0.088, 1e4, head, CNT,
+                                               SL, 16, out, pp.PP_BF16, ws, wsb, None)
+
+    assert call(B=0) == pp.PP_ERR_INVALID_ARG
+    assert call(Hkv=3) == pp.PP_ERR_INVALID_ARG
+    assert call(head=None) == pp.PP_ERR_INVALID_ARG
+    assert call(kn=None) == pp.PP_ERR_INVALID_ARG
+    assert call(v=K + B * T * Hkv * 128 * 2 - 256) == pp.PP_ERR_INVALID_ARG  # the B caches overlap
+    assert call(kn=OUT + B * P * Hq * 128 * 2 - 16) == pp.PP_ERR_INVALID_ARG  # new keys end inside out
+    assert call(head=OUT + B * P * Hq * 128 * 2 - 8) == pp.PP_ERR_INVALID_ARG  # 2B-entry head overlaps out
+    assert call(wsb=ws_bytes - 1) == pp.PP_ERR_WORKSPACE
+    assert lib.pp_last_error_message().decode() != ""
+
+
 def test_prefill_validation():
     lib = pp.raw()
     assert lib.pp_attn_prefill_workspace_bytes(0, 4, 128, pp.PP_BF16) == 0
@@ -284,6 +326,12 @@ def test_python_bindings_of_the_extensions_reject_host_tensors():
         pp.pp_attn_decode_append(q, q, q, q, q, sid, (sid[:2], sid[:2], sid[:2].view(2, 1)))
     with pytest.raises(ValueError):
         pp.pp_attn_prefill(q, q, q, sid[:2])
+    with pytest.raises(ValueError):
+        pp.pp_step_plan_multi(sid.view(1, 8), torch.zeros(1, dtype=torch.int32), 2)
+    with pytest.raises(ValueError):
+        pp.pp_attn_decode_append_multi(q.view(1, *q.shape), q.view(1, *q.shape), q.view(1, *q.shape),
+                                       q.view(1, *q.shape), q.view(1, *q.shape), sid.view(1, 8),
+                                       (sid[:2], sid[:2].view(1, 2), sid[:2].view(1, 2, 1)))
     q4 = torch.zeros(1, 2, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         pp.pp_attn_decode_multi(q4, q4, q4, sid.view(1, 8), torch.ones(1, dtype=torch.int32))
