@@ -438,7 +438,9 @@ def serving_bench(torch, pp, dev, R=16, B=4, P=16, Hq=28, Hkv=4, D=128, seed=100
     16 streams on 4k-8k-token documents, every other one asking for long
     answers (128 tokens against 8), 4 slots of one pp_attn_decode_multi
     launch per step.  Refilling a slot copies the request's cache in (a
-    stand-in for its prefill) and is inside the timed loop."""
+    stand-in for its prefill) and is inside the timed loop.  The continuous
+    schedule is also run through the appending step (one plan of all slots,
+    then append with rotation and attend), one layer per step as above."""
     import numpy as np
 
     from shared_prefix_stream_amd.batching import continuous_schedule, static_schedule
@@ -484,11 +486,41 @@ def serving_bench(torch, pp, dev, R=16, B=4, P=16, Hq=28, Hkv=4, D=128, seed=100
         torch.cuda.synchronize()
         return a.elapsed_time(e)
 
+    kn = torch.randn(B, P, Hkv, D, generator=g, device=dev, dtype=torch.bfloat16)
+    vn = torch.randn_like(kn)
+    plan = (torch.zeros(2 * B, dtype=torch.int32, device=dev), torch.zeros(B, P, dtype=torch.int32, device=dev),
+            torch.zeros(B, P, 256, dtype=torch.int32, device=dev))
+
+    def run_appending(steps):
+        # the same schedule through the appending step: per step one plan of
+        # all slots (idle slots at base -1), then append + rotate + attend
+        bases = torch.tensor([[-1 if x is None else reqs[x[0]][1] + x[1] * P for x in st] for st in steps],
+                             dtype=torch.int32, device=dev)
+        placed = [None] * B
+        torch.cuda.synchronize()
+        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i, st in enumerate(steps):
+            for b, x in enumerate(st):
+                if x is not None and placed[b] != x[0]:
+                    r = x[0]
+                    n = pool_ids[r].shape[0]
+                    K[b, :n].copy_(pool_k[r])
+                    V[b, :n].copy_(pool_v[r])
+                    sid[b, :n].copy_(pool_ids[r])
+                    placed[b] = r
+            pp.pp_step_plan_multi(sid, bases[i], P, plan=plan)
+            pp.pp_attn_decode_append_multi(q, kn, vn, K, V, sid, plan, rope_base=1e6, out=out, workspace=ws)
+        e.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(e)
+
     res = {}
-    for name, fn in (("static", static_schedule), ("continuous", continuous_schedule)):
+    for name, fn, runner in (("static", static_schedule, run), ("continuous", continuous_schedule, run),
+                             ("continuous_appending", continuous_schedule, run_appending)):
         steps = fn(answer, B)
-        run(steps)  # warm-up pass
-        ms = run(steps)
+        runner(steps)  # warm-up pass
+        ms = runner(steps)
         res[name] = {"decode_steps": len(steps), "ms": ms, "answer_tok_s": P * sum(answer) / (ms / 1e3)}
     return {"workload": f"qwen2.5-7b-heads_{R}requests_x{P}streams_{B}slots_answers8-128",
             "requests": R, "slots": B, "P": P, "Hq": Hq, "Hkv": Hkv, "doc_len": "uniform 4096-8192",
