@@ -175,3 +175,91 @@ def test_continuous_batching_loop_of_appending_steps():
             ko[n:n + P], vo[n:n + P] = ref["k_cache"][n:n + P], ref["v_cache"][n:n + P]
             ids[n:n + P] = np.arange(1, P + 1)
     say(f"  checked {len(continuous_schedule(ans, B))} steps of {len(ans)} requests in {B} slots")
+
+
+def test_multi_append_lists_past_the_plan_capacity():
+    # a plan capacity of 4 slots: the streams whose lists overflow are
+    # compacted by the gather kernel itself, up to their request's step length
+    B, P, Hq, Hkv, D, dtype, T = 2, 9, 8, 2, 128, torch.bfloat16, 1600
+    reqs = [_request(90 + b, doc, P, Hkv, D, dtype) for b, doc in enumerate([400, 1100])]
+    ids = np.zeros((B, T), dtype=np.int32)
+    k = torch.zeros(B, T, Hkv, D, dtype=dtype)
+    v = torch.zeros_like(k)
+    base = []
+    for b, (i0, k0, v0) in enumerate(reqs):
+        ids[b, :len(i0)], k[b, :len(i0)], v[b, :len(i0)] = i0, k0, v0
+        base.append(len(i0))
+    q, kn, vn = (torch.stack(x) for x in zip(*[_step_inputs(b + 7, 0, P, Hq, Hkv, D, dtype) for b in range(B)]))
+    sid, kg, vg = _i32(ids), k.to(DEV), v.to(DEV)
+    say(f"  gpu: multi append, capacity 4, base={base}")
+    plan = pp.pp_step_plan_multi(sid, _i32(base), P, tail_capacity=4)
+    out = pp.pp_attn_decode_append_multi(q.to(DEV), kn.to(DEV), vn.to(DEV), kg, vg, sid, plan, rope_base=1e4)
+    torch.cuda.synchronize()
+    counts = plan[1].cpu().numpy()
+    assert (counts > 4).sum() >= P, counts  # most lists overflow (short questions may not)
+    for b in range(B):
+        ref = oracle_append_step(q[b], kn[b], vn[b], k[b], v[b], ids[b], base[b], 1.0 / np.sqrt(D), 1e4)
+        assert_close(out[b], ref["out"], what=f"request {b}, lists past the capacity")
+
+
+def test_graph_of_the_multi_step_replays_every_step():
+    # one capture of (plan of all slots + 2 layers + advance of the busy
+    # slots), replayed 5 times; slot 1 idles throughout (base -1)
+    B, P, Hq, Hkv, D, dtype, T, L, steps = 3, 6, 4, 2, 64, torch.bfloat16, 1400, 2, 5
+    reqs = {0: _request(11, 500, P, Hkv, D, dtype), 2: _request(12, 800, P, Hkv, D, dtype)}
+
+    def setup():
+        sid = torch.zeros(B, T, dtype=torch.int32, device=DEV)
+        K = torch.zeros(L, B, T, Hkv, D, dtype=dtype, device=DEV)
+        V = torch.zeros_like(K)
+        base = torch.full((B,), -1, dtype=torch.int32, device=DEV)
+        for b, (i0, k0, v0) in reqs.items():
+            n = len(i0)
+            sid[b, :n] = _i32(i0)
+            K[:, b, :n], V[:, b, :n] = k0.to(DEV), v0.to(DEV)
+            base[b] = n
+        return sid, K, V, base
+
+    busy = _i32([1, 0, 1]) * P
+    g = torch.Generator().manual_seed(3)
+    qs = torch.randn(L, B, P, Hq, D, generator=g).to(dtype).to(DEV)
+    kvn = torch.randn(L, 2, B, P, Hkv, D, generator=g).to(dtype).to(DEV)
+    ws = torch.empty(pp.multi_workspace_bytes(T, B, P, Hq, Hkv, D, dtype), dtype=torch.uint8, device=DEV)
+    plan = (torch.zeros(2 * B, dtype=torch.int32, device=DEV), torch.zeros(B, P, dtype=torch.int32, device=DEV),
+            torch.zeros(B, P, 64, dtype=torch.int32, device=DEV))
+    outs = torch.empty(L, B, P, Hq, D, dtype=dtype, device=DEV)
+    results = {}
+    for use_graph in (False, True):
+        sid, K, V, base = setup()
+        base0 = base.clone()
+
+        def step():
+            pp.pp_step_plan_multi(sid, base, P, plan=plan)
+            for i in range(L):
+                pp.pp_attn_decode_append_multi(qs[i], kvn[i, 0], kvn[i, 1], K[i], V[i], sid, plan, rope_base=1e6,
+                                               out=outs[i], workspace=ws)
+            base.add_(busy)
+
+        graph = None
+        if use_graph:
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            say("  gpu: capture of the multi-request step")
+            with torch.cuda.graph(graph):
+                step()
+            torch.cuda.synchronize()
+            base.copy_(base0)  # capture does not run the work; the captured buffers start again
+        res = []
+        for t in range(steps):
+            if graph is not None:
+                graph.replay()
+            else:
+                step()
+            torch.cuda.synchronize()
+            res.append(outs.clone())
+        results[use_graph] = res
+        if graph is not None:
+            assert base.cpu().tolist() == [reqs[0][0].size + steps * P, -1, reqs[2][0].size + steps * P]
+    for t in range(steps):
+        assert torch.equal(results[True][t].view(torch.int16), results[False][t].view(torch.int16)), t
+        assert torch.count_nonzero(results[True][t][:, 1]).item() == 0
