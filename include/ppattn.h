@@ -267,7 +267,8 @@ pp_status_t pp_attn_decode_append(const void* q, const void* k_new, const void* 
  *   active           device int32[B][P] or NULL: 0 retires stream s of
  *                    request b (it lists nothing and its output is zero;
  *                    its new slot gets its id, but no key or value is
- *                    written there: no stream sees that slot)
+ *                    written there: no stream sees that slot); give the
+ *                    step's plan and its layers the same mask
  *   plan_head        device int32[2 * B], written: doc_len of requests
  *                    0..B-1, then their seq_len (for B = 1 the layout of
  *                    pp_step_plan)
