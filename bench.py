@@ -529,6 +529,283 @@ def serving_bench(torch, pp, dev, R=16, B=4, P=16, Hq=28, Hkv=4, D=128, seed=100
             "speedup": res["static"]["ms"] / res["continuous"]["ms"]}
 
 
+# stage of pp_attn_decode_profiled -> kernel-name prefixes in a rocprofv3 kernel trace
+STAGE_KERNELS = {
+    "plan": ("plan_kernel",),
+    "document": ("doc_mfma_bf16_kernel", "doc_valu_f32_kernel"),
+    "own_slots_merge": ("tail_merge_kernel",),
+}
+SLEEP_CYCLES = 1_000_000  # a GPU spin of ~0.5 ms: the host enqueues a timed call before the GPU reaches it
+
+
+def read_trace_avg_us(stage: str, workload: str):
+    """Average duration of a stage's kernel in profiles/kernels_<workload>.txt
+    (a rocprofv3 --kernel-trace --stats summary), or None if absent or taken
+    on other kernel sources."""
+    path = os.path.join(PROFILES, f"kernels_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    lines = open(path).read().splitlines()
+    digest = next((ln.split(":", 1)[1].strip() for ln in lines if ln.startswith("kernel_source_digest:")), None)
+    if digest != kernel_source_digest():
+        return None
+    for ln in lines:
+        if ln.startswith(STAGE_KERNELS[stage]):
+            name, rest = ln.split(">", 1) if ">" in ln else (ln.split()[0], " ".join(ln.split()[1:]))
+            cols = rest.split()
+            try:
+                return float(cols[1])  # calls, avg_us, ...
+            except (IndexError, ValueError):
+                return None
+    return None
+
+
+def median_ci(xs, n_boot: int = 2000, seed: int = 0):
+    """Median of xs and a 95 % bootstrap interval of the median."""
+    import numpy as np
+
+    a = np.asarray(xs, dtype=np.float64)
+    rng = np.random.default_rng(seed)
+    boots = np.median(a[rng.integers(0, a.size, (n_boot, a.size))], axis=1)
+    return float(np.median(a)), [float(np.percentile(boots, 2.5)), float(np.percentile(boots, 97.5))]
+
+
+def geomean_ci(xs, n_boot: int = 2000, seed: int = 1):
+    """Geometric mean of xs and a 95 % bootstrap interval of it."""
+    import numpy as np
+
+    la = np.log(np.asarray(xs, dtype=np.float64))
+    rng = np.random.default_rng(seed)
+    boots = np.exp(la[rng.integers(0, la.size, (n_boot, la.size))].mean(axis=1))
+    return float(np.exp(la.mean())), [float(np.percentile(boots, 2.5)), float(np.percentile(boots, 97.5))]
+
+
+def timed_call(torch, fn, flush=None):
+    """GPU time (ms) of one call, bracketed by events on the current stream.
+    The GPU is kept busy (a spin, or the cache-evicting write) while the host
+    enqueues the call, so host launch latency is not inside the interval."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if flush is not None:
+        flush.fill_(1)
+    else:
+        torch.cuda._sleep(SLEEP_CYCLES)
+    a.record()
+    fn()
+    b.record()
+    b.synchronize()
+    return a.elapsed_time(b)
+
+
+def paired_protocol(torch, dev, fa, fb, n_warm: int, n_cold: int):
+    """Decode step (fa) and per-question baseline (fb) on identical inputs,
+    timed as interleaved pairs (order alternating), warm and after a 1 GiB
+    cache-evicting write; medians with 95 % bootstrap intervals and the
+    geometric mean of the per-pair speedups."""
+    warm_a, warm_b, cold_a, cold_b = [], [], [], []
+    for _ in range(3):
+        fa(), fb()
+    torch.cuda.synchronize()
+    for i in range(n_warm):
+        if i % 2 == 0:
+            warm_a.append(timed_call(torch, fa))
+            warm_b.append(timed_call(torch, fb))
+        else:
+            warm_b.append(timed_call(torch, fb))
+            warm_a.append(timed_call(torch, fa))
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if n_cold else None
+    for i in range(n_cold):
+        if i % 2 == 0:
+            cold_a.append(timed_call(torch, fa, flush))
+            cold_b.append(timed_call(torch, fb, flush))
+        else:
+            cold_b.append(timed_call(torch, fb, flush))
+            cold_a.append(timed_call(torch, fa, flush))
+    del flush
+
+    def summary(xs, ys):
+        out = {}
+        if xs:
+            m, ci = median_ci(xs)
+            out.update({"median_ms": m, "ci95_ms": ci, "n": len(xs)})
+        if ys:
+            m, ci = median_ci(ys)
+            out.update({"cold_median_ms": m, "cold_ci95_ms": ci, "cold_n": len(ys)})
+        return out
+
+    res = {"decode": summary(warm_a, cold_a), "batched": summary(warm_b, cold_b),
+           "protocol": f"{n_warm} warm and {n_cold} cold interleaved pairs (order alternating) on identical inputs; "
+                       "events around each call; cold = after a 1 GiB write; medians with 95 % bootstrap intervals"}
+    if warm_a:
+        g, ci = geomean_ci([b / a for a, b in zip(warm_a, warm_b)])
+        res["speedup_geomean"], res["speedup_ci95"] = g, ci
+    if cold_a:
+        g, ci = geomean_ci([b / a for a, b in zip(cold_a, cold_b)])
+        res["cold_speedup_geomean"], res["cold_speedup_ci95"] = g, ci
+    res["batched_summary"] = {"ms_per_step": res["batched"].get("median_ms"),
+                              "speedup_of_decode": res.get("speedup_geomean"),
+                              "speedup_ci95": res.get("speedup_ci95")}
+    return res
+
+
+def read_ceiling(torch, pp, dev, gib: int = 4, reps: int = 5):
+    """Streaming-read rate of this device: a 4 GiB buffer (16x the last-level
+    cache) read whole by pp_stream_read, over a few launch widths; the best."""
+    n = gib << 30
+    buf = torch.empty(n, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    rates = {}
+    for bpc in (2, 4, 8, 16):
+        for _ in range(2):
+            pp.stream_read(buf, sink, bpc)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            pp.stream_read(buf, sink, bpc)
+        b.record()
+        torch.cuda.synchronize()
+        rates[bpc] = reps * n / (a.elapsed_time(b) / 1e3) / 1e9
+    del buf
+    torch.cuda.empty_cache()
+    best = max(rates, key=rates.get)
+    return {"gbs": rates[best], "frac_of_nominal": rates[best] / HBM_PEAK_GBS, "bytes_per_launch": n,
+            "blocks_per_cu": best, "gbs_by_blocks_per_cu": {str(k): v for k, v in rates.items()},
+            "kernel": "stream_read_kernel (include/ppmeasure.h)"}
+
+
+def read_calibration(torch, pp, steps: int):
+    """A 1 GiB buffer read `steps` times, for scaling PMC byte counters."""
+    n = 1 << 30
+    buf = torch.empty(n, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        pp.stream_read(buf, sink, 8)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    print(json.dumps({"read_bytes": n, "write_bytes": 0, "ms": ms, "gbs": n / ms / 1e6}), flush=True)
+
+
+def kernel_durations(torch, pp, case, q, k, v, sid, out, ws, n: int):
+    """Mean and median duration (us) of each stage's kernel over n profiled
+    steps, from events bound to the kernel's own start and end."""
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(pp.PP_PROFILE_EVENTS)]
+    for e in evs:
+        e.record()  # (torch creates the hipEvent_t on first record)
+    torch.cuda.synchronize()
+    handles = [e.cuda_event for e in evs]
+    per = {name: [] for name in pp.PROFILE_STAGES}
+    for _ in range(n):
+        pp.pp_attn_decode_profiled(handles, q, k, v, sid, seq_len=case.seq_len, scale=case.scale, out=out,
+                                   workspace=ws)
+        torch.cuda.synchronize()
+        for i, name in enumerate(pp.PROFILE_STAGES):
+            per[name].append(evs[2 * i].elapsed_time(evs[2 * i + 1]) * 1e3)
+    mean = {name: sum(x) / len(x) for name, x in per.items()}
+    med = {name: sorted(x)[len(x) // 2] for name, x in per.items()}
+    return mean, med
+
+
+def stage_algorithmic_bytes(by):
+    """Bytes each kernel must move (the split partials, workspace traffic, are
+    not counted)."""
+    return {
+        "plan": by["ids"],
+        "document": by["doc_kv"] + by["q"],
+        "own_slots_merge": by["tail_kv"] + by["q"] + by["out"],
+    }
+
+
+def kernel_table(stage_us, stage_med_us, stage_bytes, by):
+    kernels = {}
+    for name, us in stage_us.items():
+        gbs = stage_bytes[name] / (us * 1e-6) / 1e9
+        kernels[name] = {"us": us, "median_us": stage_med_us[name], "algorithmic_bytes": stage_bytes[name],
+                         "gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
+    doc_tflops = by["doc_flops"] / (stage_us["document"] * 1e-6) / 1e12
+    kernels["document"]["flops"] = by["doc_flops"]
+    kernels["document"]["mfma_tflops"] = doc_tflops
+    kernels["document"]["mfma_frac"] = doc_tflops / MFMA_BF16_PEAK_TFLOPS
+    return kernels
+
+
+def roofline_entry(dom, kernels, workload, ceiling):
+    """Roofline of the dominant kernel: algorithmic bytes per launch over its
+    mean duration (kernel-bound events over the profiled steps).  Its roof is
+    HBM when its flops per byte sit below the ridge of the two published
+    peaks (2.5 PFLOP/s / 8 TB/s = 312.5), else the matrix cores."""
+    kern = kernels[dom]
+    flops = kern.get("flops", 0)
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    bound = "mfma" if flops / kern["algorithmic_bytes"] > ridge else "hbm"
+    if bound == "hbm":
+        achieved, peak, unit = kern["gbs"], HBM_PEAK_GBS, "GB/s"
+    else:
+        achieved, peak, unit = kern["mfma_tflops"], MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+    trace_us = read_trace_avg_us(dom, workload)
+    entry = {
+        "bound": bound, "kernel": dom, "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
+        "traffic": read_pmc_traffic(dom, workload),
+        "algorithmic_bytes": kern["algorithmic_bytes"], "flops": flops,
+        "intensity_flop_per_byte": flops / kern["algorithmic_bytes"], "ridge_flop_per_byte": ridge,
+        "duration_us": kern["us"],
+        "achieved_from": "algorithmic bytes / mean kernel duration, HIP events bound to the kernel's start and end "
+                         "(hipExtLaunchKernel) over the profiled steps",
+        "kernel_trace_avg_us": trace_us,
+        "frac_from_kernel_trace": (kern["algorithmic_bytes"] / (trace_us * 1e-6) / 1e9 / HBM_PEAK_GBS
+                                   if trace_us and bound == "hbm" else None),
+    }
+    if flops:
+        entry["mfma_frac"] = kern["mfma_frac"]
+    if ceiling and bound == "hbm":
+        entry["measured_read_ceiling_gbs"] = ceiling["gbs"]
+        entry["frac_vs_measured"] = achieved / ceiling["gbs"]
+    return entry
+
+
+def other_config(torch, pp, dev, name, seed, steps, warmup, ceiling):
+    """One more single-step configuration, timed like the headline."""
+    from workloads import named_workload
+
+    case = named_workload(name, seed=seed)
+    q, k, v, sid = (t.to(dev) for t in (case.q, case.k, case.v, case.stream_id))
+    out = torch.empty_like(q)
+    ws = torch.empty(pp.workspace_bytes(case.seq_len, case.P, case.H, case.D, q.dtype), dtype=torch.uint8, device=dev)
+    by = step_bytes(case)
+
+    def step():
+        pp.pp_attn_decode(q, k, v, sid, seq_len=case.seq_len, scale=case.scale, out=out, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        step()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    us, med = kernel_durations(torch, pp, case, q, k, v, sid, out, ws, max(20, min(steps, 100)))
+    kv = by["doc_kv"] + by["tail_kv"]
+    step_b = kv + by["q"] + by["out"] + by["ids"]
+    res = {
+        "workload": name, "H": case.H, "d": case.D, "doc_len": case.doc_len, "P": case.P, "seq_len": case.seq_len,
+        "ms_per_step": ms, "answer_tok_s": case.P / (ms / 1e3),
+        "effective_kv_gbs": kv / (ms / 1e3) / 1e9, "effective_kv_hbm_frac": kv / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+        "step_algorithmic_bytes": step_b, "hbm_floor_us": step_b / (HBM_PEAK_GBS * 1e9) * 1e6,
+        "kernels": kernel_table(us, med, stage_algorithmic_bytes(by), by),
+    }
+    if ceiling:
+        res["effective_kv_frac_vs_measured_ceiling"] = res["effective_kv_gbs"] / ceiling["gbs"]
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -536,9 +813,6 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="codellama7b_doc16k_p256")
     ap.add_argument("--seed", type=int, default=1002)
-    ap.add_argument("--baseline-steps", type=int, default=5)
-    ap.add_argument("--cold-steps", type=int, default=20,
-                    help="steps timed after a 1 GiB cache-evicting write each (0: skip)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-batched", action="store_true")
@@ -555,6 +829,14 @@ def main():
                     help="skip the 4-request, grouped-head (28/4) decode step")
     ap.add_argument("--no-serving", action="store_true",
                     help="skip continuous against static batching of 16 requests in 4 slots")
+    ap.add_argument("--pairs", type=int, default=50,
+                    help="warm (decode step, per-question baseline) pairs timed interleaved")
+    ap.add_argument("--cold-pairs", type=int, default=20,
+                    help="the same pairs, each step after a 1 GiB cache-evicting write")
+    ap.add_argument("--no-read-ceiling", action="store_true", help="skip the streaming-read HBM ceiling")
+    ap.add_argument("--no-c2", action="store_true", help="skip the doc 8k, P = 64 step")
+    ap.add_argument("--read-calibration", action="store_true",
+                    help="only stream-read a 1 GiB buffer --steps times (to scale PMC byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -570,6 +852,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.steps)
+        return
+    if args.read_calibration:
+        read_calibration(torch, pp, args.steps)
         return
 
     dev = torch.device("cuda:0")
@@ -599,88 +884,40 @@ def main():
     ms = e0.elapsed_time(e1) / args.steps
     t_s = ms / 1e3
 
-    # ---- per-kernel durations from events the library records on its stream --
-    n_st = len(pp.PROFILE_STAGES)
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_st + 1)]
-    for e in evs:
-        e.record()
-    torch.cuda.synchronize()
-    handles = [e.cuda_event for e in evs]
-    stage_ms = [0.0] * n_st
-    n_prof = max(5, min(args.steps, 50))
-    for _ in range(n_prof):
-        pp.pp_attn_decode_profiled(handles, q, k, v, sid, seq_len=case.seq_len, scale=case.scale, out=out,
-                                   workspace=ws)
-        evs[n_st].synchronize()
-        for i in range(n_st):
-            stage_ms[i] += evs[i].elapsed_time(evs[i + 1])
-    stage_us = {name: stage_ms[i] / n_prof * 1e3 for i, name in enumerate(pp.PROFILE_STAGES)}
+    # ---- per-kernel durations: events bound to each kernel's start and end ---
+    stage_us, stage_med_us = kernel_durations(torch, pp, case, q, k, v, sid, out, ws, max(20, min(args.steps, 100)))
 
-    # ---- cold steps: 1 GiB written between steps evicts L2 and the MALL -------
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    cold = []
-    for _ in range(args.cold_steps):
-        flush.fill_(1)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        step()
-        b.record()
-        torch.cuda.synchronize()
-        cold.append(a.elapsed_time(b))
-    del flush
-    cold.sort()
-    cold_ms = cold[len(cold) // 2] if cold else None
+    # ---- paired protocol: decode step and per-question baseline interleaved --
+    outb = torch.empty_like(q)
 
-    # ---- per-question baseline on the same inputs -----------------------------
-    batched = None
+    def batched_step():
+        pp.pp_attn_decode_batched(q, k, v, sid, seq_len=case.seq_len, scale=case.scale, out=outb, workspace=ws)
+
+    paired = None
     if not args.no_batched:
-        log("bench: per-question baseline")
-        outb = torch.empty_like(q)
-        for _ in range(2):
-            pp.pp_attn_decode_batched(q, k, v, sid, seq_len=case.seq_len, scale=case.scale, out=outb, workspace=ws)
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(args.baseline_steps):
-            pp.pp_attn_decode_batched(q, k, v, sid, seq_len=case.seq_len, scale=case.scale, out=outb, workspace=ws)
-        b.record()
-        torch.cuda.synchronize()
-        bms = a.elapsed_time(b) / args.baseline_steps
-        batched = {"ms_per_step": bms, "speedup_of_decode": bms / ms,
-                   "logical_doc_reads_gb": by["doc_kv"] * case.P / 1e9,
-                   "max_abs_diff_vs_decode": float((outb.float() - out.float()).abs().max())}
+        log(f"bench: {args.pairs} warm and {args.cold_pairs} cold pairs (decode step, per-question baseline)")
+        paired = paired_protocol(torch, dev, step, batched_step, args.pairs, args.cold_pairs)
+
+    # ---- the HBM read ceiling of this device --------------------------------------
+    ceiling = None
+    if not args.no_read_ceiling:
+        log("bench: streaming-read ceiling")
+        ceiling = read_ceiling(torch, pp, dev)
 
     # ---- numbers ----------------------------------------------------------------
     kv = by["doc_kv"] + by["tail_kv"]
     kv_gbs = kv / t_s / 1e9
     doc_gbs = by["doc_kv"] / t_s / 1e9
-    # algorithmic bytes only: the split partials (fp32 workspace) are not counted
-    stage_bytes = {
-        "plan": by["ids"],
-        "document": by["doc_kv"] + by["q"],
-        "own_slots_merge": by["tail_kv"] + by["q"] + by["out"],
-    }
-    kernels = {}
-    for name, us in stage_us.items():
-        if us < 0.5:  # the stage has no launch of its own (the plain step folds the plan into its kernels)
-            kernels[name] = {"us": us, "algorithmic_bytes": stage_bytes[name], "separate_launch": False}
-            continue
-        gbs = stage_bytes[name] / (us * 1e-6) / 1e9
-        kernels[name] = {"us": us, "algorithmic_bytes": stage_bytes[name], "gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
-    doc_tflops = by["doc_flops"] / (stage_us["document"] * 1e-6) / 1e12
-    kernels["document"]["mfma_tflops"] = doc_tflops
-    kernels["document"]["mfma_frac"] = doc_tflops / MFMA_BF16_PEAK_TFLOPS
+    stage_bytes = stage_algorithmic_bytes(by)
+    kernels = kernel_table(stage_us, stage_med_us, stage_bytes, by)
     dom = max(stage_us, key=stage_us.get)
-    dom_traffic = read_pmc_traffic(dom, args.workload)
-    roofline = {
-        "bound": "hbm",
-        "kernel": dom,
-        "achieved": kernels[dom]["gbs"],
-        "peak": HBM_PEAK_GBS,
-        "unit": "GB/s",
-        "frac": kernels[dom]["gbs"] / HBM_PEAK_GBS,
-        "traffic": dom_traffic,
-    }
+    roofline = roofline_entry(dom, kernels, args.workload, ceiling)
+
+    c2 = None
+    if not args.no_c2:
+        log("bench: doc 8k, P = 64 step")
+        c2 = other_config(torch, pp, dev, "codellama7b_doc8k_p64", 1001, args.steps, args.warmup, ceiling)
+        torch.cuda.empty_cache()
 
     loop = None
     if not args.no_decode_loop:
@@ -742,7 +979,7 @@ def main():
                    "seq_len": case.seq_len, "tail_slots": by["tail_slots"], "seed": args.seed},
         "steps_per_s": 1 / t_s,
         "wall_ms_per_step": wall_ms,
-        "cold_ms_per_step": cold_ms,
+        "cold_ms_per_step": paired["decode"].get("cold_median_ms") if paired else None,
         "effective_kv_gbs": kv_gbs,
         "effective_kv_hbm_frac": kv_gbs / HBM_PEAK_GBS,
         "doc_kv_gbs": doc_gbs,
@@ -751,7 +988,11 @@ def main():
         "step_flops": by["doc_flops"] + by["tail_flops"],
         "kernels": kernels,
         "roofline": roofline,
-        "batched_baseline": batched,
+        "batched_baseline": paired["batched_summary"] if paired else None,
+        "paired": paired,
+        "hbm_read_ceiling": ceiling,
+        "effective_kv_frac_vs_measured_ceiling": (kv_gbs / ceiling["gbs"]) if ceiling else None,
+        "config_doc8k_p64": c2,
         "decode_loop": loop,
         "answer_sweep": sweep,
         "prefill": prefill,

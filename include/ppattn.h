@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define PP_ABI_VERSION 1
+#define PP_ABI_VERSION 2
 
 typedef enum {
   PP_OK = 0,
@@ -316,14 +316,14 @@ pp_status_t pp_attn_prefill(const void* q, const void* k, const void* v, const i
 
 /* Profiling variant of pp_attn_decode (batched == 0) or pp_attn_decode_batched
  * (batched != 0): identical arguments, contract and results, and it also
- * records caller-created hipEvent_t events on hip_stream around its kernel
- * launches, so each stage can be timed with hipEventElapsedTime on the stream
- * the kernels actually run on.  events[0] is recorded before the first
- * launch and events[i] right after the i-th; the stages, in launch order,
- * are: visibility plan, document part, own-slot gather + merge.  Needs
- * n_events >= PP_PROFILE_EVENTS (else PP_ERR_INVALID_ARG); a failed event
- * record is PP_ERR_HIP. */
-#define PP_PROFILE_EVENTS 4
+ * binds caller-created hipEvent_t events to the start and the end of each of
+ * its kernels (hipExtLaunchKernel), so that hipEventElapsedTime(events[2i],
+ * events[2i + 1]) is the execution time of stage i's kernel alone, on the
+ * stream the kernels run on.  The stages, in launch order, are: visibility
+ * plan, document part, own-slot gather + merge.  Needs n_events >=
+ * PP_PROFILE_EVENTS (else PP_ERR_INVALID_ARG); a failed launch is
+ * PP_ERR_HIP. */
+#define PP_PROFILE_EVENTS 6
 pp_status_t pp_attn_decode_profiled(int32_t batched, const void* q, const void* k_cache, const void* v_cache,
                                     const int32_t* stream_id, int64_t seq_len, int32_t P, int32_t H, int32_t d,
                                     float scale, void* out, pp_dtype_t dtype, void* workspace,
@@ -331,7 +331,7 @@ pp_status_t pp_attn_decode_profiled(int32_t batched, const void* q, const void* 
                                     int32_t n_events);
 
 /* The integer visibility plan that both entry points evaluate on the device
- * (their first kernel), exposed for inspection: the same device code.
+ * (their first kernels), exposed for inspection: the same device code.
  * Writes, on `hip_stream`:
  *   doc_len_out[0]      length of the leading run of id-0 slots (<= seq_len)
  *   tail_count_out[s]   number of slots j >= doc_len visible to stream s
@@ -339,11 +339,16 @@ pp_status_t pp_attn_decode_profiled(int32_t batched, const void* q, const void* 
  *   tail_slots_out[s*tail_capacity + i]  the first min(count, tail_capacity)
  *                       of those slots, ascending
  * All three are caller-owned device buffers (int32; tail_slots_out may be
- * NULL when tail_capacity is 0).  `workspace` (at least
- * PP_PLAN_WORKSPACE_BYTES, caller-owned device memory) is reserved: it is
- * checked but not written.  [Project page, "How it works", item 1.]
- * Errors as above. */
+ * NULL when tail_capacity is 0).  `workspace` is caller-owned device
+ * scratch of at least pp_attn_plan_workspace_bytes(seq_len, P) bytes (never
+ * less than PP_PLAN_WORKSPACE_BYTES); it must not overlap stream_id or the
+ * outputs (PP_ERR_INVALID_ARG).  For P <= 1024 the plan is built in two
+ * passes over chunks of the ids (per-chunk counts of every stream's id, then
+ * each visible slot placed at its rank in slot order), O(seq_len) work in
+ * all; larger P take one pass per stream over all ids.  [Project page, "How
+ * it works", item 1.]  Errors as above. */
 #define PP_PLAN_WORKSPACE_BYTES 512
+size_t pp_attn_plan_workspace_bytes(int64_t seq_len, int32_t P);
 pp_status_t pp_attn_plan(const int32_t* stream_id, int64_t seq_len, int32_t P,
                          int32_t* doc_len_out, int32_t* tail_count_out, int32_t* tail_slots_out,
                          int64_t tail_capacity, void* workspace, size_t workspace_bytes, void* hip_stream);

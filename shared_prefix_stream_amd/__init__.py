@@ -49,6 +49,7 @@ __all__ = [
     "pp_attn_prefill",
     "multi_workspace_bytes",
     "pp_attn_decode_multi",
+    "stream_read",
     "PP_OK",
     "PP_ERR_INVALID_ARG",
     "PP_ERR_UNSUPPORTED",
@@ -130,6 +131,10 @@ def _load():
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, f32, vp, ctypes.c_int, vp, sz, vp]
+    lib.pp_attn_plan_workspace_bytes.restype = sz
+    lib.pp_attn_plan_workspace_bytes.argtypes = [i64, i32]
+    lib.pp_stream_read.restype = ctypes.c_int
+    lib.pp_stream_read.argtypes = [vp, sz, vp, i32, vp]
     _lib = lib
     return lib
 
@@ -264,15 +269,15 @@ def pp_attn_decode_planned(q, k_cache, v_cache, stream_id, plan, seq_len: Option
     return out
 
 
-PP_PROFILE_EVENTS = 4
+PP_PROFILE_EVENTS = 6
 PROFILE_STAGES = ("plan", "document", "own_slots_merge")
 
 
 def pp_attn_decode_profiled(events, q, k_cache, v_cache, stream_id, seq_len: Optional[int] = None,
                             scale: Optional[float] = None, out=None, workspace=None, batched: bool = False):
     """pp_attn_decode (or the batched baseline) with raw hipEvent_t handles
-    recorded around each kernel launch: events[0] before the plan kernel,
-    events[i] after the i-th of (plan, document, own-slot gather + merge)."""
+    bound to the start and end of each kernel: events[2i], events[2i + 1]
+    bracket the i-th of (plan, document, own-slot gather + merge)."""
     P, H, d, seq_len, scale, code, out, workspace = _prepare(q, k_cache, v_cache, stream_id, seq_len, scale, out,
                                                              workspace)
     arr = (ctypes.c_void_p * len(events))(*events)
@@ -295,7 +300,7 @@ def pp_attn_plan(stream_id, seq_len: int, P: int, tail_capacity: int = 0) -> Tup
     doc_len = torch.empty(1, dtype=torch.int32, device=dev)
     counts = torch.empty(P, dtype=torch.int32, device=dev)
     slots = torch.full((P, max(tail_capacity, 1)), -1, dtype=torch.int32, device=dev)
-    ws = torch.empty(PP_PLAN_WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
+    ws = torch.empty(int(_load().pp_attn_plan_workspace_bytes(int(seq_len), int(P))), dtype=torch.uint8, device=dev)
     st = _load().pp_attn_plan(stream_id.data_ptr(), int(seq_len), int(P), doc_len.data_ptr(), counts.data_ptr(),
                               slots.data_ptr(), int(tail_capacity), ws.data_ptr(), ws.numel(), _stream_handle(dev))
     _check(st)
@@ -597,3 +602,16 @@ def pp_attn_decode_multi(q, k_cache, v_cache, stream_id, seq_lens, scale: Option
               Hq, Hkv, d, scale, out.data_ptr(), code, workspace.data_ptr(),
               workspace.numel() * workspace.element_size(), _stream_handle(q.device)))
     return out
+
+
+def stream_read(buf, sink, blocks_per_cu: int = 8) -> None:
+    """Read every byte of the contiguous GPU tensor `buf` once on the current
+    stream (measurement aid, include/ppmeasure.h); `sink` is a GPU int32 or
+    uint32 tensor of at least one element."""
+    if not buf.is_cuda or not sink.is_cuda:
+        raise ValueError("stream_read needs GPU tensors")
+    if not buf.is_contiguous():
+        raise ValueError("buf must be contiguous")
+    nbytes = buf.numel() * buf.element_size()
+    _check(_load().pp_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), int(blocks_per_cu),
+                                  _stream_handle(buf.device)))

@@ -8,6 +8,10 @@
 
 #include "pp_internal.h"
 
+namespace pp {
+thread_local StageEvents g_stage_events;
+}
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -187,29 +191,38 @@ pp_status_t decode_impl(Path path, const void* q, const void* k, const void* v, 
   }
   if (ap && !bt.seq_lens) ws.dyn_len = xp->doc_len + 1;  // {doc_len, seq_len} of the step
 
-  // optional profiling events around the launches
-  auto mark = [&](int i) -> hipError_t {
-    return events ? hipEventRecord(static_cast<hipEvent_t>(events[i]), stream) : hipSuccess;
+  // optional profiling: stage i's kernel is bound to events[2i] (its start)
+  // and events[2i + 1] (its end)
+  auto stage = [&](int i) {
+    if (events)
+      pp::g_stage_events = {static_cast<hipEvent_t>(events[2 * i]), static_cast<hipEvent_t>(events[2 * i + 1])};
   };
-  hipError_t e = mark(0);
-  if (e == hipSuccess && !xp) e = pp::launch_plan(sid, seq_len, P, ws.plan, ws.counts, ws.slots, ws.cap, stream, bt);
+  auto unstage = [&]() { pp::g_stage_events = pp::StageEvents(); };
+  hipError_t e = hipSuccess;
+  if (!xp) {
+    stage(0);
+    e = pp::launch_plan(sid, seq_len, P, ws.plan, ws.counts, ws.slots, ws.cap, stream, bt, ws.rows);
+    unstage();
+  }
   if (e == hipSuccess && ap) {  // new keys and values into the caches, rotated queries into the workspace
     e = pp::launch_append_rope(q, ap->k_new, ap->v_new, const_cast<void*>(k), const_cast<void*>(v), P, H, Hkv, d, dtype,
                                ap->rope_base, ws.plan, ws.counts, seq_len, ws.q_rot, stream, B, bt.kv_stride,
                                bt.active);
     q = ws.q_rot;
   }
-  if (e == hipSuccess) e = mark(1);
   if (e == hipSuccess) {
+    stage(1);
     e = path == Path::kParallel
             ? pp::launch_doc(pl.doc, q, k, v, seq_len, P, Hkv, d, dtype, c, ws, stream, false, bt)
             : pp::launch_batched_doc(n_splits, q, k, v, seq_len, P, H, d, dtype, c, ws, stream, bt);
+    unstage();
   }
-  if (e == hipSuccess) e = mark(2);
-  if (e == hipSuccess)
+  if (e == hipSuccess) {
+    stage(2);
     e = pp::launch_tail_merge(n_splits, q, k, v, sid, seq_len, P, H, d, dtype, c, ws, out, stream, bt);
-  if (e == hipSuccess) e = mark(3);
-  if (e != hipSuccess) return fail(PP_ERR_HIP, "kernel launch or event record failed: %s", hipGetErrorString(e));
+    unstage();
+  }
+  if (e != hipSuccess) return fail(PP_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 
@@ -245,9 +258,23 @@ pp_status_t check_prefill_shape(int64_t seq_len, int32_t H, int32_t d, pp_dtype_
   return PP_OK;
 }
 
+// Scratch of pp_attn_plan: the two-pass plan's chunk rows (and the base
+// alignment), at least PP_PLAN_WORKSPACE_BYTES.
+size_t plan_scratch_bytes(int64_t seq_len, int32_t P) {
+  const size_t r = pp::plan_rows_bytes(seq_len, P, 1);
+  const size_t n = r ? 256 + r : 0;
+  return n > PP_PLAN_WORKSPACE_BYTES ? n : (size_t)PP_PLAN_WORKSPACE_BYTES;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t pp_attn_plan_workspace_bytes(int64_t seq_len, int32_t P) {
+  if (seq_len < 1 || seq_len > PP_MAX_SEQ_LEN || P < 1 || P > PP_MAX_STREAMS) return 0;
+  ok();
+  return plan_scratch_bytes(seq_len, P);
+}
 
 int pp_abi_version(void) { return PP_ABI_VERSION; }
 
@@ -497,13 +524,22 @@ pp_status_t pp_attn_plan(const int32_t* stream_id, int64_t seq_len, int32_t P, i
   if (tail_capacity < 0 || (tail_capacity > 0 && !tail_slots_out))
     return fail(PP_ERR_INVALID_ARG, "tail_slots_out is null or tail_capacity negative");
   if (!aligned16(stream_id)) return fail(PP_ERR_INVALID_ARG, "stream_id must be 16-byte aligned");
-  if (!workspace || workspace_bytes < PP_PLAN_WORKSPACE_BYTES)
-    return fail(PP_ERR_WORKSPACE, "pp_attn_plan needs %d bytes of workspace", (int)PP_PLAN_WORKSPACE_BYTES);
+  const size_t need = plan_scratch_bytes(seq_len, P);
+  if (!workspace || workspace_bytes < need)
+    return fail(PP_ERR_WORKSPACE, "pp_attn_plan needs %zu bytes of workspace", need);
+  const size_t nid = (size_t)seq_len * 4, nc = (size_t)P * 4, ns = (size_t)P * (size_t)tail_capacity * 4;
+  if (overlaps(workspace, workspace_bytes, stream_id, nid) || overlaps(workspace, workspace_bytes, doc_len_out, 4) ||
+      overlaps(workspace, workspace_bytes, tail_count_out, nc) ||
+      overlaps(workspace, workspace_bytes, tail_slots_out, ns))
+    return fail(PP_ERR_INVALID_ARG, "workspace overlaps stream_id or an output");
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-  // the workspace argument is reserved: the plan is written straight into
-  // the caller's buffers
+  // the workspace holds the per-chunk rows of the two-pass plan; the plan
+  // itself is written straight into the caller's buffers
+  int32_t* rows = pp::plan_rows_bytes(seq_len, P, 1)
+                      ? reinterpret_cast<int32_t*>(pp::align_up((uintptr_t)workspace, 256))
+                      : nullptr;
   hipError_t e = pp::launch_plan(stream_id, seq_len, P, doc_len_out, tail_count_out, tail_slots_out, tail_capacity,
-                                 stream);
+                                 stream, pp::Batch(), rows);
   if (e != hipSuccess) return fail(PP_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }

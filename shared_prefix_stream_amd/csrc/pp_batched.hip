@@ -179,18 +179,12 @@ hipError_t launch_batched_doc(int n_splits, const void* q, const void* k, const 
                               const Batch& bt) {
   const dim3 grid(H, n_splits, P * bt.B);  // dispatch order: heads, then splits, stream outermost
 #define PP_B_LAUNCH(TT, DD)                                                                                   \
-  batched_doc_kernel<TT, DD><<<grid, kBThreads, 0, stream>>>(static_cast<const TT*>(q), static_cast<const TT*>(k), \
-                                                             static_cast<const TT*>(v), P, H, c, ws.plan,    \
-                                                             seq_len, n_splits, ws.part_o, ws.part_ml, bt)
-  if (dtype == PP_BF16) {
-    if (d == 128) PP_B_LAUNCH(uint16_t, 128);
-    else PP_B_LAUNCH(uint16_t, 64);
-  } else {
-    if (d == 128) PP_B_LAUNCH(float, 128);
-    else PP_B_LAUNCH(float, 64);
-  }
+  launch_kernel(batched_doc_kernel<TT, DD>, grid, dim3(kBThreads), stream, static_cast<const TT*>(q),           \
+                static_cast<const TT*>(k), static_cast<const TT*>(v), P, H, c, ws.plan, seq_len, n_splits,      \
+                ws.part_o, ws.part_ml, bt)
+  if (dtype == PP_BF16) return d == 128 ? PP_B_LAUNCH(uint16_t, 128) : PP_B_LAUNCH(uint16_t, 64);
+  return d == 128 ? PP_B_LAUNCH(float, 128) : PP_B_LAUNCH(float, 64);
 #undef PP_B_LAUNCH
-  return hipGetLastError();
 }
 
 }  // namespace pp

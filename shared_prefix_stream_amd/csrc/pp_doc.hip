@@ -347,10 +347,11 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
 
   // ---- online softmax of tile t (base 2, lazy rescale) -> packed P^T --------
   uint32_t pb[QB][CH][4];  // P^T as packed bf16 pairs: the P.V B operand
-  auto softmax = [&](int t) __attribute__((always_inline)) {
+  // Scaled scores of keys outside the visible range set to -inf: the split's
+  // ragged last tile, or (CAUSAL) keys past a query.  Taken only on tiles
+  // that have such keys (wave-uniform test).
+  auto mask_tile = [&](int t) __attribute__((always_inline)) {
     const int kbase = t * NK;
-    // ragged last tile of the split, or (CAUSAL) a tile with keys past the
-    // wave's first query (uniform)
     if (__builtin_expect(kbase + NK > key_end || (CAUSAL && kbase + NK - 1 > q0), 0)) {
       // the empty asm keeps this rare block a branch: without it the compiler
       // turns the masking into compares and selects run on every tile
@@ -365,6 +366,15 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
             if (kbase + key >= key_end || (CAUSAL && kbase + key > q0 + qb * 16 + ln)) s[qb][kb][i] = -INFINITY;
           }
     }
+  };
+  auto softmax = [&](int t) __attribute__((always_inline)) {
+    // scaled scores x = s * |c| first, the mask after: a masked key is
+    // x = -inf whatever the scale (scaling -inf by a zero scale would be NaN)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) s[qb][kb] *= cabs;
+    mask_tile(t);
     // running maxima: lane (query ln, group lg) holds 4*KB keys of its query;
     // reduce over the 4 groups with lane swaps
     float tmax[QB];
@@ -376,8 +386,7 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) smax = fmaxf(smax, s[qb][kb][i]);
-      smax = max_xor32(max_xor16(smax));
-      tmax[qb] = smax * cabs;
+      tmax[qb] = max_xor32(max_xor16(smax));
       grow |= tmax[qb] > m[qb] + kLazyTau;
     }
     if (__builtin_expect(__builtin_amdgcn_ballot_w64(grow) != 0, 0)) {  // wave-uniform, rare after the first tile
@@ -398,7 +407,7 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s[qb][kb][i] = fast_exp2(fmaf(s[qb][kb][i], cabs, mneg));
+        for (int i = 0; i < 4; ++i) s[qb][kb][i] = fast_exp2(s[qb][kb][i] + mneg);
 #pragma unroll
       for (int ch = 0; ch < CH; ++ch) {
         pb[qb][ch][0] = pack_bf16x2(s[qb][2 * ch][0], s[qb][2 * ch][1]);
@@ -411,19 +420,11 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
 
   // fast pass: p = exp2(x) with the fixed reference 0
   auto softmax_fast = [&](int t) __attribute__((always_inline)) {
-    const int kbase = t * NK;
-    if (__builtin_expect(kbase + NK > key_end || (CAUSAL && kbase + NK - 1 > q0), 0)) {  // as in softmax
-      asm volatile("" ::: "memory");  // (kept a branch, as in softmax)
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = 32 * (kb >> 1) + 8 * lg + 4 * (kb & 1) + i;
-            if (kbase + key >= key_end || (CAUSAL && kbase + key > q0 + qb * 16 + ln)) s[qb][kb][i] = -INFINITY;
-          }
-    }
+      for (int kb = 0; kb < KB; ++kb) s[qb][kb] *= cabs;  // scaled first, masked after (as in softmax)
+    mask_tile(t);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -431,8 +432,8 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
         float pv_[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          pv_[i] = fast_exp2(s[qb][2 * ch][i] * cabs);
-          pv_[4 + i] = fast_exp2(s[qb][2 * ch + 1][i] * cabs);
+          pv_[i] = fast_exp2(s[qb][2 * ch][i]);
+          pv_[4 + i] = fast_exp2(s[qb][2 * ch + 1][i]);
         }
         pb[qb][ch][0] = pack_bf16x2(pv_[0], pv_[1]);
         pb[qb][ch][1] = pack_bf16x2(pv_[2], pv_[3]);
@@ -755,20 +756,19 @@ hipError_t launch_doc(const DocPlan& pl, const void* q, const void* k, const voi
     auto* kk = static_cast<const uint16_t*>(k);
     auto* vv = static_cast<const uint16_t*>(v);
 #define PP_DOC_LAUNCH(DD, QQ, WW)                                                                           \
-  (causal ? doc_mfma_bf16_kernel<DD, QQ, WW, true><<<grid, 64 * WW, 0, stream>>>(                                 \
-                qq, kk, vv, P, H, c, ws.plan, seq_len, pl.n_splits, ws.part_o, ws.part_ml, bt,                   \
-                static_cast<uint16_t*>(out))                                                                 \
-          : doc_mfma_bf16_kernel<DD, QQ, WW, false><<<grid, 64 * WW, 0, stream>>>(                                \
-                qq, kk, vv, P, H, c, ws.plan, seq_len, pl.n_splits, ws.part_o, ws.part_ml, bt, nullptr))
+  (causal ? launch_kernel(doc_mfma_bf16_kernel<DD, QQ, WW, true>, grid, dim3(64 * WW), stream, qq, kk, vv, P, H, \
+                          c, ws.plan, seq_len, pl.n_splits, ws.part_o, ws.part_ml, bt, static_cast<uint16_t*>(out)) \
+          : launch_kernel(doc_mfma_bf16_kernel<DD, QQ, WW, false>, grid, dim3(64 * WW), stream, qq, kk, vv, P,    \
+                          H, c, ws.plan, seq_len, pl.n_splits, ws.part_o, ws.part_ml, bt, nullptr))
     // dispatch on the exact (d, 16-query blocks per wave, waves) triple
     const int cfg = d * 10000 + pl.qb * 100 + pl.nw;
     switch (cfg) {
-      case 1280104: PP_DOC_LAUNCH(128, 1, 4); break;
-      case 1280204: PP_DOC_LAUNCH(128, 2, 4); break;
-      case 1280208: PP_DOC_LAUNCH(128, 2, 8); break;
-      case 640104: PP_DOC_LAUNCH(64, 1, 4); break;
-      case 640204: PP_DOC_LAUNCH(64, 2, 4); break;
-      case 640208: PP_DOC_LAUNCH(64, 2, 8); break;
+      case 1280104: return PP_DOC_LAUNCH(128, 1, 4);
+      case 1280204: return PP_DOC_LAUNCH(128, 2, 4);
+      case 1280208: return PP_DOC_LAUNCH(128, 2, 8);
+      case 640104: return PP_DOC_LAUNCH(64, 1, 4);
+      case 640204: return PP_DOC_LAUNCH(64, 2, 4);
+      case 640208: return PP_DOC_LAUNCH(64, 2, 8);
       default: return hipErrorInvalidConfiguration;
     }
 #undef PP_DOC_LAUNCH
@@ -776,18 +776,13 @@ hipError_t launch_doc(const DocPlan& pl, const void* q, const void* k, const voi
     auto* qq = static_cast<const float*>(q);
     auto* kk = static_cast<const float*>(k);
     auto* vv = static_cast<const float*>(v);
-#define PP_F32_LAUNCH(DD, CC) \
-  doc_valu_f32_kernel<DD, CC><<<grid, kDocThreads, 0, stream>>>(qq, kk, vv, P, H, c, ws.plan, seq_len, pl.n_splits, ws.part_o, ws.part_ml, bt, static_cast<float*>(out))
-    if (d == 128) {
-      if (causal) PP_F32_LAUNCH(128, true);
-      else PP_F32_LAUNCH(128, false);
-    } else {
-      if (causal) PP_F32_LAUNCH(64, true);
-      else PP_F32_LAUNCH(64, false);
-    }
+#define PP_F32_LAUNCH(DD, CC)                                                                                \
+  launch_kernel(doc_valu_f32_kernel<DD, CC>, grid, dim3(kDocThreads), stream, qq, kk, vv, P, H, c, ws.plan, seq_len, \
+                pl.n_splits, ws.part_o, ws.part_ml, bt, static_cast<float*>(out))
+    if (d == 128) return causal ? PP_F32_LAUNCH(128, true) : PP_F32_LAUNCH(128, false);
+    return causal ? PP_F32_LAUNCH(64, true) : PP_F32_LAUNCH(64, false);
 #undef PP_F32_LAUNCH
   }
-  return hipGetLastError();
 }
 
 }  // namespace pp

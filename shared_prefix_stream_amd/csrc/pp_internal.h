@@ -2,12 +2,44 @@
 // gfx950 (CDNA4) only: 64-wide wavefronts, MFMA bf16 16x16x32, 160 KB LDS.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <tuple>
+#include <utility>
 
 #include "ppattn.h"
 
 namespace pp {
+
+// ------------------------------------------------------------ launching ---
+// Events that the next kernel launch of this host thread binds to its own
+// start and end (hipExtLaunchKernel), so that hipEventElapsedTime gives that
+// kernel's execution time alone; both null for ordinary launches.  Set only
+// by the profiling entry point around one launch at a time.
+struct StageEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+extern thread_local StageEvents g_stage_events;
+
+template <typename Tup, size_t... I>
+inline void kernel_arg_ptrs(Tup& t, void** argv, std::index_sequence<I...>) {
+  ((argv[I] = (void*)&std::get<I>(t)), ...);
+}
+
+// Launch of kernel k (no dynamic LDS) with its arguments converted to the
+// kernel's parameter types; returns the launch status.
+template <typename... Params, typename... Args>
+inline hipError_t launch_kernel(void (*k)(Params...), dim3 grid, dim3 block, hipStream_t stream, Args&&... args) {
+  static_assert(sizeof...(Params) == sizeof...(Args), "kernel argument count");
+  std::tuple<Params...> t(std::forward<Args>(args)...);
+  void* argv[sizeof...(Params) > 0 ? sizeof...(Params) : 1];
+  kernel_arg_ptrs(t, argv, std::index_sequence_for<Params...>{});
+  const StageEvents ev = g_stage_events;
+  return hipExtLaunchKernel(reinterpret_cast<const void*>(k), grid, block, argv, 0, stream, ev.start, ev.stop, 0);
+}
 
 // Lazy rescaling threshold (log2 units): the running maximum used as the
 // softmax reference is only raised when a score (or a tile's maximum)
@@ -65,6 +97,7 @@ __device__ __forceinline__ int64_t request_len(const Batch& bt, int b, int64_t b
 //   [.., +O)          float  part_o [n_splits][P][H][d] (unnormalised)
 //   [.., +QR)         the step's rotated queries [P][H][d] (appending step
 //                     only; room for 4-byte elements)
+//   [.., +RW)         the two-pass plan's chunk rows (plan_rows_bytes)
 struct Workspace {
   int32_t* plan;
   int32_t* counts;
@@ -73,6 +106,7 @@ struct Workspace {
   float2* part_ml;
   float* part_o;
   void* q_rot;
+  int32_t* rows = nullptr;  // two-pass plan scratch (null: P too large for it)
   // appending step: the step's length lives on the device (plan[1]); the
   // host-side seq_len is then only an upper bound
   const int32_t* dyn_len = nullptr;
@@ -90,6 +124,37 @@ inline int64_t list_cap_for(int64_t seq_len) {
 
 inline size_t plan_bytes_for(int64_t B) { return align_up((size_t)(B < 2 ? 2 : B) * 4, 256); }
 
+// Two-pass plan: the ids are cut into at most 64 chunks of a multiple of 1024
+// slots; each chunk gets a head of kRowHead ints (first non-zero id, zero
+// ids, zero ids after the first non-zero one, -) and the count of each
+// stream's id.
+constexpr int kRowMaxP = 1024;  // streams per request the two-pass plan handles
+constexpr int kRowHead = 4;
+inline int plan_row_chunks(int64_t seq_len) {
+  const int64_t n = (seq_len + 1023) / 1024;
+  return (int)(n < 1 ? 1 : (n > 64 ? 64 : n));
+}
+inline int64_t plan_row_chunk_len(int64_t seq_len) {
+  const int64_t nc = plan_row_chunks(seq_len);
+  const int64_t per = (seq_len + nc - 1) / nc;
+  return (per + 1023) / 1024 * 1024;
+}
+// chunks per request rounded up to a multiple of 4: per request the rows
+// are [stride][kRowHead] chunk heads then [P][stride] per-stream counts, so
+// each stream's counts over all chunks are a few 16-byte loads
+__host__ __device__ inline int plan_row_stride(int nc) { return (nc + 3) & ~3; }
+// Which plan a launch takes.  The two passes are two small launches, each
+// with a fixed cost of ~5 us on an MI355X whatever its work (measured: 5 us
+// to count 32 chunks, 9 us to place them, at 16k + 15k slots and 256
+// streams), while one workgroup per stream over all ids costs ~10 us there
+// but grows with P x seq_len; past 2^24 stream-slots the two passes win.
+inline bool use_two_pass_plan(int64_t seq_len, int64_t P) {
+  return P <= kRowMaxP && P * seq_len > ((int64_t)1 << 24);
+}
+inline size_t plan_rows_bytes(int64_t seq_len, int64_t P, int64_t B) {
+  return P > kRowMaxP ? 0 : align_up((size_t)B * plan_row_stride(plan_row_chunks(seq_len)) * (P + kRowHead) * 4, 256);
+}
+
 // P: streams of the launch (all requests), H: query heads.
 inline size_t workspace_bytes_for(int n_splits, int64_t P, int64_t H, int64_t d, int64_t seq_len, int64_t B = 1) {
   const size_t cnt = align_up((size_t)P * 4, 256);
@@ -97,7 +162,8 @@ inline size_t workspace_bytes_for(int n_splits, int64_t P, int64_t H, int64_t d,
   const size_t ml = align_up((size_t)n_splits * P * H * sizeof(float2), 256);
   const size_t o = align_up((size_t)n_splits * P * H * d * sizeof(float), 256);
   const size_t qr = align_up((size_t)P * H * d * 4, 256);
-  return 256 /*base alignment slack*/ + plan_bytes_for(B) + cnt + sl + ml + o + qr;
+  const size_t rw = plan_rows_bytes(seq_len, P / B, B);
+  return 256 /*base alignment slack*/ + plan_bytes_for(B) + cnt + sl + ml + o + qr + rw;
 }
 
 inline Workspace carve_workspace(void* ws, int n_splits, int64_t P, int64_t H, int64_t d, int64_t seq_len,
@@ -116,6 +182,8 @@ inline Workspace carve_workspace(void* ws, int n_splits, int64_t P, int64_t H, i
   w.part_o = reinterpret_cast<float*>(at);
   at += align_up((size_t)n_splits * P * H * d * sizeof(float), 256);
   w.q_rot = reinterpret_cast<void*>(at);
+  at += align_up((size_t)P * H * d * 4, 256);
+  w.rows = plan_rows_bytes(seq_len, P / B, B) ? reinterpret_cast<int32_t*>(at) : nullptr;
   return w;
 }
 
@@ -292,9 +360,11 @@ __device__ int collect_visible(const int32_t* __restrict__ sid, int64_t from, in
 
 // Visibility plan: doc_len into plan[0]; for every stream s, the number of
 // slots j in [doc_len, seq_len) it sees (counts[s]) and the first cap of
-// them in ascending order (slots[s*cap ...]).  One workgroup per stream.
+// them in ascending order (slots[s*cap ...]).  With `rows` (plan_rows_bytes
+// of scratch) and P <= kRowMaxP: two passes over chunks of the ids, O(T)
+// work; otherwise one workgroup per stream over all ids.
 hipError_t launch_plan(const int32_t* sid, int64_t seq_len, int P, int32_t* plan, int32_t* counts, int32_t* slots,
-                       int64_t cap, hipStream_t stream, const Batch& bt = Batch());
+                       int64_t cap, hipStream_t stream, const Batch& bt = Batch(), int32_t* rows = nullptr);
 
 // The same for a decode step that appends one slot per stream: the step
 // starts at *base_len (device), stream s's new slot is *base_len + s and gets

@@ -184,13 +184,283 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
   }
 }
 
+// ------------------------------------------------------------------------------
+// Two-pass plan, O(T) work in total (P <= kRowMaxP).  The ids are cut into NC
+// chunks of CH slots (CH a multiple of 1024); a workgroup of 4 waves handles
+// one chunk of one request, in sub-chunks of 1024 slots where wave w, column
+// e, lane l holds slot c0 + sub + 256 w + 64 e + l (coalesced dword loads).
+//
+// Pass 1 (plan_count_kernel) writes, per chunk (slots < length only):
+//   a head: the offset in the chunk of its first non-zero id (CH if none),
+//   its zero ids, its zero ids after that first non-zero one;
+//   for s in [1, P] the number of its ids s, at cnt[s - 1][chunk] (the
+//   counts of one stream over all chunks are contiguous).
+// Pass 2 (plan_scatter_kernel), chunk c: the document prefix ends at the
+// first non-zero id of the first chunk that has one; a zero id past it is a
+// late document slot, visible to every stream.  A visible slot j of stream
+// s sits in s's ascending list at
+//   (own slots of s before j) + (late document slots before j),
+// the part before the chunk summed from the rows of earlier chunks, the part
+// inside from a rank among the chunk's slots with the same id: within a
+// column of 64 lanes by ballots over the id's bits (the lanes holding the
+// same id, and how many of them come first), across columns by a per-wave
+// running count, across waves by a prefix over the 4 per-wave counts.
+// Ranks only follow slot order: no atomic decides a position.  A chunk with
+// late document slots takes a plain ordered walk over its ids per stream
+// instead (late document slots are rare: the configurations never place one).
+constexpr int kRowThreads = 256;  // 4 waves
+constexpr int kRowSub = 1024;     // slots per sub-chunk
+
+// Lanes of the wave whose x equals this lane's (x in [0, 2^nbits)).
+__device__ __forceinline__ uint64_t same_lanes(int x, int nbits) {
+  uint64_t m = ~0ull;
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = ((x >> b) & 1) != 0;
+    const uint64_t bb = __builtin_amdgcn_ballot_w64(bit);
+    m &= bit ? bb : ~bb;
+  }
+  return m;
+}
+
+__global__ __launch_bounds__(kRowThreads) void plan_count_kernel(const int32_t* __restrict__ sid, int64_t seq_len,
+                                                                 int P, int nc, int64_t ch,
+                                                                 int32_t* __restrict__ rows, Batch bt) {
+  __shared__ int hist[kRowMaxP + 1];
+  __shared__ int first, zsum;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = blockIdx.x, b = blockIdx.y;
+  sid += b * bt.id_stride;
+  const int64_t len = request_len(bt, b, seq_len);
+  const int64_t c0 = (int64_t)c * ch;
+  const int nbits = 32 - __builtin_clz((unsigned)P);
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int i = tid; i <= P; i += kRowThreads) hist[i] = 0;
+  if (tid == 0) {
+    first = 0x7fffffff;
+    zsum = 0;
+  }
+  __syncthreads();
+  int zeros = 0;  // (wave-uniform) zero ids this wave saw
+  for (int64_t sub = 0; sub < ch && c0 + sub < len; sub += kRowSub) {
+    const int64_t wb = c0 + sub + 256 * wave;
+    int id[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t j = wb + 64 * e + lane;
+      id[e] = j < len ? sid[j] : 0;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool valid = wb + 64 * e + lane < len;
+      const uint64_t nz = __builtin_amdgcn_ballot_w64(valid && id[e] != 0);
+      if (nz != 0 && lane == 0) atomicMin(&first, (int)(sub + 256 * wave + 64 * e + __builtin_ctzll(nz)));
+      zeros += __popcll(__builtin_amdgcn_ballot_w64(valid && id[e] == 0));
+      const bool own = valid && id[e] >= 1 && id[e] <= P;
+      const int x = own ? id[e] : 0;
+      const uint64_t m = same_lanes(x, nbits);
+      if (own && (m & below) == 0) atomicAdd(&hist[x], __popcll(m));  // one lane per id: counts only
+    }
+  }
+  if (lane == 0) atomicAdd(&zsum, zeros);
+  __syncthreads();
+  const int ncp = plan_row_stride(nc);
+  int32_t* head = rows + (int64_t)b * ncp * (P + kRowHead);
+  if (tid == 0) {
+    const int f = first;
+    const int32_t fo = f == 0x7fffffff ? (int32_t)ch : f;
+    // the zeros before the first non-zero id are all of [c0, c0 + f)
+    *reinterpret_cast<int4*>(head + (int64_t)c * kRowHead) =
+        make_int4(fo, zsum, f == 0x7fffffff ? 0 : zsum - f, 0);
+  }
+  int32_t* cnt = head + (int64_t)ncp * kRowHead;
+  for (int i = tid; i < P; i += kRowThreads) {
+    cnt[(int64_t)i * ncp + c] = hist[i + 1];
+    if (c == 0)  // the padding chunks of the stride count nothing
+      for (int p = nc; p < ncp; ++p) cnt[(int64_t)i * ncp + p] = 0;
+  }
+}
+
+__global__ __launch_bounds__(kRowThreads) void plan_scatter_kernel(
+    const int32_t* __restrict__ sid, int64_t seq_len, int P, int nc, int64_t ch, const int32_t* __restrict__ rows,
+    int32_t* __restrict__ plan, int32_t* __restrict__ counts, int32_t* __restrict__ slots, int64_t cap, Batch bt) {
+  __shared__ int offs[4][kRowMaxP + 1];  // per wave: running count of each id, then its offsets
+  __shared__ int base[kRowMaxP + 1];     // own slots of each stream before the current sub-chunk
+  __shared__ int live[kRowMaxP + 1];
+  __shared__ int ids_l[kRowSub];
+  __shared__ int64_t head[5];            // document chunk, late slots before / in / over all chunks, doc_len
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = blockIdx.x, b = blockIdx.y;
+  sid += b * bt.id_stride;
+  const int64_t len = request_len(bt, b, seq_len);
+  const int64_t c0 = (int64_t)c * ch;
+  const int nbits = 32 - __builtin_clz((unsigned)P);
+  const uint64_t below = (1ull << lane) - 1ull;
+  const int ncp = plan_row_stride(nc);
+  const int32_t* head_b = rows + (int64_t)b * ncp * (P + kRowHead);  // [ncp][4] chunk heads
+  const int32_t* cnt_b = head_b + (int64_t)ncp * kRowHead;          // [P][ncp] per-stream counts
+  // Every load that does not depend on another is issued first: this
+  // chunk's first 1024 ids, the heads of all chunk rows (wave 0) and the
+  // per-stream counts of all chunks (nc <= 64, so one batch per stream).
+  int id0[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int64_t j = c0 + 256 * wave + 64 * e + lane;
+    id0[e] = j < len ? sid[j] : 0;
+  }
+  int f = (int)ch, za = 0, zf = 0;
+  if (wave == 0 && lane < nc) {
+    const int4 h = *reinterpret_cast<const int4*>(head_b + lane * kRowHead);
+    f = h.x;
+    za = h.y;
+    zf = h.z;
+  }
+  for (int s = tid + 1; s <= P; s += kRowThreads) {
+    live[s] = (!bt.active || bt.active[b * P + s - 1] != 0) ? 1 : 0;  // (per thread: not wave-uniform)
+    const int4* col = reinterpret_cast<const int4*>(cnt_b + (int64_t)(s - 1) * ncp);
+    int4 v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = 4 * i < ncp ? col[i] : make_int4(0, 0, 0, 0);
+    // (padding entries are zero; chunk index compared on the vector unit)
+    const int cv = c + (tid & 0x80000000);
+    int own_before = 0, own_all = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int e[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        own_before += 4 * i + u < cv ? e[u] : 0;
+        own_all += e[u];
+      }
+    }
+    base[s] = own_before;
+    if (c == 0) counts[b * P + s - 1] = live[s] ? own_all : 0;  // (the late total is added below)
+  }
+  if (wave == 0) {
+    // document chunk: the first chunk with a non-zero id; late document slots
+    // of chunk i: none before it, those after its first non-zero id in it,
+    // all its zero ids after it
+    const uint64_t has = __builtin_amdgcn_ballot_w64(lane < nc && f < ch);
+    const int cd = has ? __builtin_ctzll(has) : nc;
+    const int late = (lane < nc && lane >= cd) ? (lane == cd ? zf : za) : 0;
+    int pre = lane < c ? late : 0, tot = late;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {  // wave sums
+      pre += __shfl_xor(pre, o);
+      tot += __shfl_xor(tot, o);
+    }
+    const int mine = __shfl(late, c < 64 ? c : 0);
+    const int fcd = __shfl(f, cd < nc ? cd : 0);  // (wave 0 holds every chunk head)
+    if (lane == 0) {
+      const int64_t dl = cd < nc ? min<int64_t>((int64_t)cd * ch + fcd, len) : len;
+      head[0] = cd;
+      head[1] = pre;
+      head[2] = mine;
+      head[3] = tot;
+      head[4] = dl;
+      if (c == 0) plan[b] = (int32_t)dl;
+    }
+  }
+  __syncthreads();
+  const int late_before = (int)head[1], late_here = (int)head[2], late_all = (int)head[3];
+  const int64_t doc_len = head[4];
+  if (c == 0 && late_all > 0)
+    for (int s = tid + 1; s <= P; s += kRowThreads)
+      if (live[s]) counts[b * P + s - 1] += late_all;
+  if (c0 + ch <= doc_len || c0 >= len) return;  // the chunk is document only, or past the length
+  if (late_here == 0) {
+    for (int64_t sub = 0; sub < ch && c0 + sub < len; sub += kRowSub) {
+      for (int s = lane + 1; s <= P; s += 64) offs[wave][s] = 0;  // this wave's row
+      const int64_t wb = c0 + sub + 256 * wave;
+      int x[4], r[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t j = wb + 64 * e + lane;
+        const int id = sub == 0 ? id0[e] : (j < len ? sid[j] : 0);
+        const bool own = j < len && j >= doc_len && id >= 1 && id <= P;
+        x[e] = (own && live[id]) ? id : 0;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint64_t m = same_lanes(x[e], nbits);
+        const int before_in_wave = x[e] ? offs[wave][x[e]] : 0;
+        r[e] = before_in_wave + __popcll(m & below);
+        if (x[e] && (m & below) == 0) offs[wave][x[e]] = before_in_wave + __popcll(m);
+      }
+      __syncthreads();
+      for (int s = tid + 1; s <= P; s += kRowThreads) {  // per stream: offsets of the 4 waves
+        int run = base[s];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int t = offs[w][s];
+          offs[w][s] = run;
+          run += t;
+        }
+        base[s] = run;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (x[e]) {
+          const int64_t pos = (int64_t)late_before + offs[wave][x[e]] + r[e];
+          if (pos < cap) slots[((int64_t)b * P + x[e] - 1) * cap + pos] = (int32_t)(wb + 64 * e + lane);
+        }
+      }
+      __syncthreads();  // offs[] is cleared for the next sub-chunk
+    }
+  } else {
+    // ordered walk: every stream scans the chunk's ids in slot order
+    int late_run = late_before;
+    for (int64_t sub = 0; sub < ch && c0 + sub < len; sub += kRowSub) {
+      for (int i = tid; i < kRowSub; i += kRowThreads) {
+        const int64_t j = c0 + sub + i;
+        ids_l[i] = j < len ? sid[j] : -1;
+      }
+      __syncthreads();
+      const int n = (int)min<int64_t>(kRowSub, len - (c0 + sub));
+      for (int s = tid + 1; s <= P; s += kRowThreads) {
+        if (!live[s]) continue;
+        int64_t pos = (int64_t)base[s] + late_run;
+        int own = 0;
+        for (int i = 0; i < n; ++i) {
+          const int64_t j = c0 + sub + i;
+          const int id = ids_l[i];
+          if (j >= doc_len && (id == 0 || id == s)) {
+            if (pos < cap) slots[((int64_t)b * P + s - 1) * cap + pos] = (int32_t)j;
+            ++pos;
+            own += id == s;
+          }
+        }
+        base[s] += own;
+      }
+      int z = 0;  // late document slots of this sub-chunk (every thread counts them)
+      for (int i = 0; i < n; ++i) z += (c0 + sub + i >= doc_len && ids_l[i] == 0) ? 1 : 0;
+      late_run += z;
+      __syncthreads();  // ids_l[] is refilled
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_plan(const int32_t* sid, int64_t seq_len, int P, int32_t* plan, int32_t* counts, int32_t* slots,
-                       int64_t cap, hipStream_t stream, const Batch& bt) {
-  plan_kernel<false><<<dim3(P, bt.B), kPlanThreads, 0, stream>>>(sid, seq_len, plan, counts, slots, cap, nullptr,
-                                                                 nullptr, bt);
-  return hipGetLastError();
+                       int64_t cap, hipStream_t stream, const Batch& bt, int32_t* rows) {
+  if (rows && use_two_pass_plan(seq_len, P)) {
+    const int nc = plan_row_chunks(seq_len);
+    const int64_t ch = plan_row_chunk_len(seq_len);
+    // a profiled launch: the stage runs from the first pass's start to the second's end
+    const StageEvents ev = g_stage_events;
+    g_stage_events = {ev.start, nullptr};
+    hipError_t e = launch_kernel(plan_count_kernel, dim3(nc, bt.B), dim3(kRowThreads), stream, sid, seq_len, P, nc,
+                                 ch, rows, bt);
+    g_stage_events = {nullptr, ev.stop};
+    if (e == hipSuccess)
+      e = launch_kernel(plan_scatter_kernel, dim3(nc, bt.B), dim3(kRowThreads), stream, sid, seq_len, P, nc, ch, rows,
+                        plan, counts, slots, cap, bt);
+    g_stage_events = ev;
+    return e;
+  }
+  return launch_kernel(plan_kernel<false>, dim3(P, bt.B), dim3(kPlanThreads), stream, sid, seq_len, plan, counts,
+                       slots, cap, nullptr, nullptr, bt);
 }
 
 hipError_t launch_plan_append(int32_t* sid, const int32_t* base_len, int64_t max_len, int P, int32_t* plan,

@@ -298,10 +298,9 @@ hipError_t launch_tail_t(int n_splits, const void* q, const void* k, const void*
                          int tile = 0, const Batch& bt = Batch()) {
   using S = TailShape<T, D>;
   const dim3 grid(P * bt.B, (H + S::GW - 1) / S::GW);
-  tail_merge_kernel<T, D, PREFILL><<<grid, kTailThreads, 0, stream>>>(
-      static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), sid, seq_len, P, H, c, ws.plan,
-      ws.counts, ws.slots, ws.cap, n_splits, ws.part_o, ws.part_ml, static_cast<T*>(out), ws.dyn_len, tile, bt);
-  return hipGetLastError();
+  return launch_kernel(tail_merge_kernel<T, D, PREFILL>, grid, dim3(kTailThreads), stream, static_cast<const T*>(q),
+                       static_cast<const T*>(k), static_cast<const T*>(v), sid, seq_len, P, H, c, ws.plan, ws.counts,
+                       ws.slots, ws.cap, n_splits, ws.part_o, ws.part_ml, static_cast<T*>(out), ws.dyn_len, tile, bt);
 }
 
 }  // namespace

@@ -1,5 +1,5 @@
 """The C ABI on a machine without a GPU: the library loads, exports every
-symbol include/ppattn.h declares, and rejects bad arguments on the host
+symbol the headers under include/ declare, and rejects bad arguments on the host
 before any HIP call (only fake, never-dereferenced pointers are passed)."""
 import ctypes
 import math
@@ -10,16 +10,21 @@ import pytest
 
 import shared_prefix_stream_amd as pp
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "ppattn.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include")
+HEADER = os.path.join(INCLUDE, "ppattn.h")
 
 # fake device addresses, 16-byte aligned and far apart
 Q, K, V, SID, OUT, WS = (0x10000000 * i for i in range(1, 7))
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pp_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in sorted(os.listdir(INCLUDE)):
+        if h.endswith(".h"):
+            text = open(os.path.join(INCLUDE, h)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(pp_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_function():
@@ -30,12 +35,12 @@ def test_library_exports_every_declared_function():
                           "pp_attn_prefill", "pp_attn_prefill_workspace_bytes", "pp_attn_decode_multi",
                           "pp_attn_decode_multi_batched", "pp_attn_multi_workspace_bytes", "pp_abi_version", "pp_status_string", "pp_last_error_message"}
     for n in names:
-        assert hasattr(lib, n), f"{n} declared in ppattn.h but not exported"
+        assert hasattr(lib, n), f"{n} declared in include/ but not exported"
 
 
 def test_abi_version_and_status_strings():
     lib = pp.raw()
-    assert pp.abi_version() == 1
+    assert pp.abi_version() == 2
     for code in range(5):
         assert lib.pp_status_string(code).decode().startswith("PP_")
     assert b"unknown" in lib.pp_status_string(99)
@@ -107,7 +112,7 @@ def test_profiled_validation():
     assert call(with_null, pp.PP_PROFILE_EVENTS) == pp.PP_ERR_INVALID_ARG
     # the decode arguments are still checked
     assert call(ev, pp.PP_PROFILE_EVENTS, P=0) == pp.PP_ERR_INVALID_ARG
-    assert len(pp.PROFILE_STAGES) == pp.PP_PROFILE_EVENTS - 1
+    assert 2 * len(pp.PROFILE_STAGES) == pp.PP_PROFILE_EVENTS
     text = open(HEADER).read()
     assert re.search(r"#define PP_PROFILE_EVENTS %d\b" % pp.PP_PROFILE_EVENTS, text)
 
@@ -346,3 +351,31 @@ def test_bench_refuses_several_gpus():
                        cwd=root, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in r.stderr
+
+
+def test_stream_read_validation():
+    lib = pp.raw()
+    # null, misaligned, empty or ragged sizes, blocks per CU out of range: rejected before any HIP call
+    assert lib.pp_stream_read(None, 1024, OUT, 8, None) == pp.PP_ERR_INVALID_ARG
+    assert lib.pp_stream_read(Q + 8, 1024, OUT, 8, None) == pp.PP_ERR_INVALID_ARG
+    assert lib.pp_stream_read(Q, 0, OUT, 8, None) == pp.PP_ERR_INVALID_ARG
+    assert lib.pp_stream_read(Q, 1000, OUT, 8, None) == pp.PP_ERR_INVALID_ARG
+    assert lib.pp_stream_read(Q, 1024, None, 8, None) == pp.PP_ERR_INVALID_ARG
+    assert lib.pp_stream_read(Q, 1024, OUT, 0, None) == pp.PP_ERR_INVALID_ARG
+    assert lib.pp_stream_read(Q, 1024, OUT, 65, None) == pp.PP_ERR_INVALID_ARG
+
+
+def test_plan_workspace_bytes():
+    lib = pp.raw()
+    # chunk rows of the two-pass plan: at most 64 chunks of P + 4 ints, never below the fixed minimum
+    assert lib.pp_attn_plan_workspace_bytes(10, 2) == pp.PP_PLAN_WORKSPACE_BYTES
+    n = lib.pp_attn_plan_workspace_bytes(31825, 256)
+    assert n >= 32 * (256 + 4) * 4 and n < 64 * (256 + 4) * 4 + 1024
+    assert lib.pp_attn_plan_workspace_bytes(1 << 20, 1024) >= 64 * (1024 + 4) * 4
+    assert lib.pp_attn_plan_workspace_bytes(1000, 5000) == pp.PP_PLAN_WORKSPACE_BYTES  # one pass per stream
+    assert lib.pp_attn_plan_workspace_bytes(0, 2) == 0 and lib.pp_attn_plan_workspace_bytes(10, 0) == 0
+    # a workspace below the size for the shape is rejected
+    big = lib.pp_attn_plan_workspace_bytes(31825, 256)
+    assert lib.pp_attn_plan(SID, 31825, 256, OUT, WS, K, 4, V, big - 1, None) == pp.PP_ERR_WORKSPACE
+    # a workspace over the ids is rejected
+    assert lib.pp_attn_plan(SID, 31825, 256, OUT, WS, K, 4, SID, big, None) == pp.PP_ERR_INVALID_ARG

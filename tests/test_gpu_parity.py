@@ -3,7 +3,7 @@
 Tolerance: max |gpu - oracle| <= 2e-2 over all elements and, per (stream,
 head) row, max |gpu - oracle| / max |oracle| <= 1e-2 (bf16 inputs, fp32
 accumulation).  Small shapes are checked on every stream; the full-size
-workloads on sampled streams (all heads)."""
+headline workload (doc 16k, P = 256) on every stream as well."""
 import numpy as np
 import pytest
 import torch
@@ -56,7 +56,6 @@ def test_doc8k_p64_all_streams(entry):
 
 
 @pytest.mark.parametrize("entry", ["decode", "batched"])
-def test_doc16k_p256_sampled_streams(entry):
+def test_doc16k_p256_all_streams(entry):
     case = named_workload("codellama7b_doc16k_p256", seed=1002)
-    streams = [0, 1, 2, 63, 64, 127, 128, 200, 254, 255]
-    assert_close(run(case, entry), reference(case, streams), streams, what=case.name)
+    assert_close(run(case, entry), reference(case), what=case.name)

@@ -240,6 +240,17 @@ def test_zero_keys_give_mean_of_visible_values():
         np.testing.assert_allclose(out[s], v[sel].mean(axis=0), rtol=0, atol=1e-14)
 
 
+@pytest.mark.parametrize("scale", [0.0, -0.0])
+def test_zero_scale_gives_mean_of_visible_values(scale):
+    # every visible logit is 0 whatever the keys: the uniform softmax over V_s
+    c = _small_case(16, P=5, doc=23)
+    v = c.v.double().numpy()
+    out = oracle_decode(c.q, c.k, v, c.stream_id.numpy(), c.seq_len, scale)
+    for s in range(c.P):
+        sel = np.concatenate([np.arange(c.doc_len), c.own_slots[s]]).astype(np.int64)
+        np.testing.assert_allclose(out[s], v[sel].mean(axis=0), rtol=0, atol=1e-14)
+
+
 def test_constant_values_give_that_constant():
     c = _small_case(7)
     v = np.broadcast_to(np.array([0.25 * i - 1 for i in range(c.D)]), c.v.shape).copy()
