@@ -113,6 +113,23 @@ pp_status_t pp_attn_decode(const void* q, const void* k_cache, const void* v_cac
                            int32_t d, float scale, void* out, pp_dtype_t dtype, void* workspace,
                            size_t workspace_bytes, void* hip_stream);
 
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc:
+ * pp_attn_decode without a workspace argument.  Its workspace is a fixed
+ * scratch array of the library in each GPU's memory,
+ * PP_NOALLOC_SCRATCH_BYTES per GPU, held from the library's load until the
+ * process ends; the call itself allocates nothing.  Shapes whose
+ * pp_attn_workspace_bytes exceeds that size are rejected with
+ * PP_ERR_WORKSPACE.  Every call on one GPU uses the same array: calls that
+ * overlap on a GPU (other streams, other host threads) race and must be
+ * serialized by the caller.  Arguments, results and the other errors as
+ * pp_attn_decode (PP_ERR_HIP also if the array's device address cannot be
+ * obtained). */
+#define PP_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+pp_status_t pp_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* stream_id, int64_t seq_len, int32_t P, int32_t H,
+                                   int32_t d, float scale, void* out, pp_dtype_t dtype, void* hip_stream);
+
 /* The same result computed as P independent requests ("batched requests",
  * one request per question, as a stock serving engine runs them): every
  * stream reads the whole document's K/V for itself with a per-query

@@ -37,6 +37,7 @@ __all__ = [
     "workspace_bytes",
     "pp_attn_decode",
     "pp_attn_decode_batched",
+    "pp_attn_decode_noalloc",
     "pp_attn_plan",
     "pp_attn_decode_profiled",
     "PROFILE_STAGES",
@@ -131,6 +132,8 @@ def _load():
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, f32, vp, ctypes.c_int, vp, sz, vp]
+    lib.pp_attn_decode_noalloc.restype = ctypes.c_int
+    lib.pp_attn_decode_noalloc.argtypes = [vp, vp, vp, vp, i64, i32, i32, i32, f32, vp, ctypes.c_int, vp]
     lib.pp_attn_plan_workspace_bytes.restype = sz
     lib.pp_attn_plan_workspace_bytes.argtypes = [i64, i32]
     lib.pp_stream_read.restype = ctypes.c_int
@@ -241,6 +244,25 @@ def pp_attn_decode_batched(q, k_cache, v_cache, stream_id, seq_len: Optional[int
                            scale: Optional[float] = None, out=None, workspace=None):
     """The same step as P independent per-question requests (the baseline)."""
     return _decode("pp_attn_decode_batched", q, k_cache, v_cache, stream_id, seq_len, scale, out, workspace)
+
+
+PP_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def pp_attn_decode_noalloc(q, k_cache, v_cache, stream_id, seq_len: Optional[int] = None,
+                           scale: Optional[float] = None, out=None):
+    """pp_attn_decode with the library's fixed per-GPU scratch array as its
+    workspace (no allocation in the call; calls overlapping on one GPU race)."""
+    import torch
+
+    if out is None:
+        out = torch.empty_like(q)
+    P, H, d, seq_len, scale, code, out, _ = _prepare(q, k_cache, v_cache, stream_id, seq_len, scale, out,
+                                                     torch.empty(0, dtype=torch.uint8, device=q.device))
+    st = _load().pp_attn_decode_noalloc(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), stream_id.data_ptr(),
+                                        seq_len, P, H, d, scale, out.data_ptr(), code, _stream_handle(q.device))
+    _check(st)
+    return out
 
 
 def pp_attn_decode_planned(q, k_cache, v_cache, stream_id, plan, seq_len: Optional[int] = None,

@@ -13,6 +13,15 @@ thread_local StageEvents g_stage_events;
 }
 
 namespace {
+pp_status_t fail(pp_status_t st, const char* fmt, ...);
+}
+
+namespace pp {
+// (for the other translation units: the calling thread's error message)
+pp_status_t set_error(pp_status_t st, const char* msg) { return fail(st, "%s", msg); }
+}
+
+namespace {
 
 thread_local char g_err[512] = "";
 

@@ -24,6 +24,9 @@ struct StageEvents {
 };
 extern thread_local StageEvents g_stage_events;
 
+// Sets the calling thread's pp_last_error_message() and returns st.
+pp_status_t set_error(pp_status_t st, const char* msg);
+
 template <typename Tup, size_t... I>
 inline void kernel_arg_ptrs(Tup& t, void** argv, std::index_sequence<I...>) {
   ((argv[I] = (void*)&std::get<I>(t)), ...);

@@ -379,3 +379,17 @@ def test_plan_workspace_bytes():
     assert lib.pp_attn_plan(SID, 31825, 256, OUT, WS, K, 4, V, big - 1, None) == pp.PP_ERR_WORKSPACE
     # a workspace over the ids is rejected
     assert lib.pp_attn_plan(SID, 31825, 256, OUT, WS, K, 4, SID, big, None) == pp.PP_ERR_INVALID_ARG
+
+
+def test_noalloc_rejects_shapes_beyond_its_scratch_on_the_host():
+    lib = pp.raw()
+    T, P, H, d = 40000, 1024, 64, 128
+    assert lib.pp_attn_workspace_bytes(T, P, H, d, pp.PP_BF16) > pp.PP_NOALLOC_SCRATCH_BYTES
+    assert lib.pp_attn_decode_noalloc(Q, K, V, SID, T, P, H, d, 0.088, OUT, pp.PP_BF16, None) == pp.PP_ERR_WORKSPACE
+    assert b"fixed scratch" in lib.pp_last_error_message()
+    # an invalid shape gets the decode step's own status
+    assert lib.pp_attn_decode_noalloc(Q, K, V, SID, 0, 8, 4, 128, 0.088, OUT, pp.PP_BF16, None) == pp.PP_ERR_INVALID_ARG
+    assert lib.pp_attn_decode_noalloc(Q, K, V, SID, 100, 8, 4, 96, 0.088, OUT, pp.PP_BF16, None) == pp.PP_ERR_UNSUPPORTED
+    text = open(HEADER).read()
+    assert re.search(r"#define PP_NOALLOC_SCRATCH_BYTES \(\(size_t\)64 << 20\)", text)
+    assert pp.PP_NOALLOC_SCRATCH_BYTES == 64 << 20
