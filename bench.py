@@ -16,7 +16,7 @@ dominant kernel, the per-question baseline's time on the same inputs, and
 the fp64 CPU oracle timed on a bounded sample of streams.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
-    python bench.py --copy-calibration   # plain 1 GiB copy, to scale PMC byte counters
+    python bench.py --read-calibration   # 1 GiB streaming read, to scale PMC byte counters
 """
 from __future__ import annotations
 
@@ -153,24 +153,6 @@ def _cpu_model():
     except OSError:
         pass
     return "unknown"
-
-
-def copy_calibration(steps: int):
-    import torch
-
-    n = 1 << 30
-    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
-    dst = torch.empty_like(src)
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(steps):
-        dst.copy_(src)
-    b.record()
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / steps
-    print(json.dumps({"copy_bytes": n, "read_bytes": n, "write_bytes": n, "ms": ms,
-                      "gbs_read_plus_write": 2 * n / ms / 1e6}), flush=True)
 
 
 def decode_loop(torch, pp, dev, layers=32, steps=32, doc=12000, P=256, H=32, D=128, seed=1003, rope_base=1e6,
@@ -816,7 +798,6 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-batched", action="store_true")
-    ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-decode-loop", action="store_true",
                     help="skip the 32-step x 32-layer appending loop (eager and graph-replayed)")
     ap.add_argument("--decode-loop-heads", choices=("both", "mha", "grouped"), default="both",
@@ -850,9 +831,6 @@ def main():
     import shared_prefix_stream_amd as pp
     from workloads import named_workload
 
-    if args.copy_calibration:
-        copy_calibration(args.steps)
-        return
     if args.read_calibration:
         read_calibration(torch, pp, args.steps)
         return
