@@ -216,9 +216,8 @@ def _prepare(q, k_cache, v_cache, stream_id, seq_len, scale, out, workspace):
         out = torch.empty_like(q)
     elif out.shape != q.shape or out.dtype != q.dtype or not out.is_cuda or not out.is_contiguous():
         raise ValueError("out must be a contiguous GPU tensor shaped and typed like q")
-    need = workspace_bytes(seq_len, P, H, d, code)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is None:  # (a caller's workspace is checked by the library itself)
+        workspace = torch.empty(workspace_bytes(seq_len, P, H, d, code), dtype=torch.uint8, device=q.device)
     return P, H, d, int(seq_len), float(scale), code, out, workspace
 
 
