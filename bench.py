@@ -542,6 +542,32 @@ def read_trace_avg_us(stage: str, workload: str):
     return None
 
 
+def read_sq_counters(stage: str, workload: str):
+    """Matrix-core busy and LDS utilisation of a stage's kernel from
+    profiles/pmc_sq_<workload>.txt (rocprofv3 SQ counters), or None if absent
+    or taken on other kernel sources."""
+    path = os.path.join(PROFILES, f"pmc_sq_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    lines = open(path).read().splitlines()
+    digest = next((ln.split(":", 1)[1].strip() for ln in lines if ln.startswith("kernel_source_digest:")), None)
+    if digest != kernel_source_digest():
+        return None
+    out, inside = {}, False
+    for ln in lines:
+        if ln and not ln.startswith(" ") and not ln.startswith("#"):
+            inside = ln.startswith(stage + " (")
+            continue
+        if inside and "%" in ln and "=" in ln:
+            key = ln.split("=")[0].strip()
+            if key in ("MfmaUtil", "LdsUtil"):
+                out[key] = float(ln.rsplit(None, 2)[-2]) / 100.0
+    if not out:
+        return None
+    out["source"] = os.path.relpath(path, ROOT)
+    return out
+
+
 def median_ci(xs, n_boot: int = 2000, seed: int = 0):
     """Median of xs and a 95 % bootstrap interval of the median."""
     import numpy as np
@@ -744,6 +770,9 @@ def roofline_entry(dom, kernels, workload, ceiling):
     }
     if flops:
         entry["mfma_frac"] = kern["mfma_frac"]
+    # what the counters say binds it below both roofs (the roofline's bound is
+    # the lower roof at this intensity)
+    entry["counters"] = read_sq_counters(dom, workload)
     if ceiling and bound == "hbm":
         entry["measured_read_ceiling_gbs"] = ceiling["gbs"]
         entry["frac_vs_measured"] = achieved / ceiling["gbs"]

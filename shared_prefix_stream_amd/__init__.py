@@ -78,7 +78,9 @@ class PPError(RuntimeError):
 
 
 def library_path() -> str:
-    return os.path.join(_HERE, _LIB_NAME)
+    """The in-tree libppattn.so, or the library PP_ATTN_LIBRARY names (for
+    instance an AddressSanitizer build of the host code)."""
+    return os.environ.get("PP_ATTN_LIBRARY") or os.path.join(_HERE, _LIB_NAME)
 
 
 def _load():
