@@ -116,13 +116,19 @@ def cpu_baseline(case, target_s: float):
     a = max(t1 - b * n1, 0.0)
     n = int(max(n2, min(case.P, (target_s - a) / b)))
     dt = timed(n)
+    passes = 1
+    # a whole step shorter than the target: repeat it (whole steps) up to about the target
+    while n == case.P and dt * (passes + 1) / passes <= target_s:
+        dt += timed(n)
+        passes += 1
     threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    what = f"{n} of {case.P} streams" if passes == 1 else f"the whole step ({n} streams) {passes} times"
     return {
-        "value": n / dt,
+        "value": n * passes / dt,
         "unit": "answer tok/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{n} of {case.P} streams x all {case.H} heads of the same step, fp64 NumPy, {dt:.1f} s "
+        "sample": f"{what} x all {case.H} heads, fp64 NumPy, {dt:.1f} s "
                   f"(includes the oracle's fp64 conversion of the KV cache)",
         "seconds": dt,
         "cpu_model": _cpu_model(),
