@@ -38,7 +38,8 @@
  * Ownership and asynchrony: the library allocates no memory.  Scratch space
  * is the caller's `workspace` (device memory of at least
  * pp_attn_workspace_bytes(...) bytes, 16-byte aligned).  Work is enqueued on
- * `hip_stream` (a hipStream_t; NULL = the null stream) and the call returns
+ * `hip_stream` (a hipStream_t of the current device; NULL = the null
+ * stream) and the call returns
  * without waiting and without reading device data on the host.  Inputs,
  * `out` and `workspace` must stay valid until the stream has passed the
  * call.  Two calls that run at the same time must not share a workspace.
@@ -122,7 +123,9 @@ pp_status_t pp_attn_decode(const void* q, const void* k_cache, const void* v_cac
  * pp_attn_workspace_bytes exceeds that size are rejected with
  * PP_ERR_WORKSPACE.  Every call on one GPU uses the same array: calls that
  * overlap on a GPU (other streams, other host threads) race and must be
- * serialized by the caller.  Arguments, results and the other errors as
+ * serialized by the caller.  The array used is the current device's:
+ * a non-null hip_stream of another device is rejected with
+ * PP_ERR_INVALID_ARG.  Arguments, results and the other errors as
  * pp_attn_decode (PP_ERR_HIP also if the array's device address cannot be
  * obtained). */
 #define PP_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)

@@ -54,6 +54,14 @@ extern "C" pp_status_t pp_attn_decode_noalloc(const void* q, const void* k_cache
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
     return pp::set_error(PP_ERR_HIP, "could not get the current device");
+  // the scratch used is the current device's: a stream of another device
+  // would run the step against memory of the wrong GPU
+  if (hip_stream) {
+    int sdev = -1;
+    if (hipStreamGetDevice(static_cast<hipStream_t>(hip_stream), &sdev) != hipSuccess)
+      return pp::set_error(PP_ERR_HIP, "could not get the stream's device");
+    if (sdev != dev) return pp::set_error(PP_ERR_INVALID_ARG, "hip_stream belongs to another device than the current one");
+  }
   hipError_t e = hipSuccess;
   void* ws = scratch_address(dev, &e);
   if (!ws) {
