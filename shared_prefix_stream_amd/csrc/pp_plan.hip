@@ -87,32 +87,47 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
 #pragma unroll
     for (int g = 0; g < kPlanG; ++g) {
       const int64_t jg = wb + 4 * (64 * g + lane);
-      const int64_t jl = jg < last_gran ? jg : last_gran;
-      x[g] = *reinterpret_cast<const int4*>(sid + jl);
-      if constexpr (APPEND) {
-        x[g].x = jl >= app ? (int)(jl - app) + 1 : x[g].x;
-        x[g].y = jl + 1 >= app ? (int)(jl + 1 - app) + 1 : x[g].y;
-        x[g].z = jl + 2 >= app ? (int)(jl + 2 - app) + 1 : x[g].z;
-        x[g].w = jl + 3 >= app ? (int)(jl + 3 - app) + 1 : x[g].w;
+      x[g] = *reinterpret_cast<const int4*>(sid + (jg < last_gran ? jg : last_gran));
+    }
+    if constexpr (APPEND) {
+      // the step's new slots [app, seq_len) hold their streams' ids whatever
+      // memory holds (uniform test: only the rows that reach them)
+#pragma unroll
+      for (int g = 0; g < kPlanG; ++g) {
+        if (wb + 256 * (g + 1) > app) {
+          const int64_t jg = wb + 4 * (64 * g + lane);
+          const int64_t jl = jg < last_gran ? jg : last_gran;
+          x[g].x = jl >= app ? (int)(jl - app) + 1 : x[g].x;
+          x[g].y = jl + 1 >= app ? (int)(jl + 1 - app) + 1 : x[g].y;
+          x[g].z = jl + 2 >= app ? (int)(jl + 2 - app) + 1 : x[g].z;
+          x[g].w = jl + 3 >= app ? (int)(jl + 3 - app) + 1 : x[g].w;
+        }
       }
     }
-    // slot wb + 4*(64g + lane) + e is valid iff 4*(64g + lane) + e < hi
+    // slot wb + 4*(64g + lane) + e is valid iff 4*(64g + lane) + e < hi; row
+    // g holds the wave's slots [256g, 256g + 256) (offsets from wb)
     const int hi = (int)max<int64_t>(min<int64_t>(seq_len - wb, kPlanWaveSpan), 0);
+    // non-zero ids among the lane's valid slots of row g, one bit per slot
+    auto nz_bits = [&](int g) __attribute__((always_inline)) {
+      const unsigned valid = (1u << min(max(hi - 4 * (64 * g + lane), 0), 4)) - 1u;
+      return (((unsigned)(x[g].x != 0)) | ((unsigned)(x[g].y != 0) << 1) | ((unsigned)(x[g].z != 0) << 2) |
+              ((unsigned)(x[g].w != 0) << 3)) & valid;
+    };
     // 1. document prefix
     if (doc_len < 0) {
       // this wave's first non-zero id: the first row whose ballot is
-      // non-empty, its first lane, then that lane's first element
+      // non-empty, its first lane, then that lane's first slot; rows come in
+      // slot order, so the search stops at the first such row
       int first = 0x7fffffff;
 #pragma unroll
       for (int g = 0; g < kPlanG; ++g) {
-        const int r0 = 4 * (64 * g + lane);
-        const unsigned valid = (1u << min(max(hi - r0, 0), 4)) - 1u;
-        const unsigned nz = (((unsigned)(x[g].x != 0)) | ((unsigned)(x[g].y != 0) << 1) |
-                             ((unsigned)(x[g].z != 0) << 2) | ((unsigned)(x[g].w != 0) << 3)) & valid;
-        const uint64_t b = __builtin_amdgcn_ballot_w64(nz != 0);
-        if (first == 0x7fffffff && b != 0) {  // uniform
-          const int l0 = __builtin_ctzll(b);
-          first = 4 * (64 * g + l0) + __builtin_ctz((unsigned)__builtin_amdgcn_readlane((int)nz, l0));
+        if (first != 0x7fffffff) break;  // (uniform)
+        // a row with every slot valid needs no per-slot test (uniform choice)
+        const bool any = 256 * (g + 1) <= hi ? (x[g].x | x[g].y | x[g].z | x[g].w) != 0 : nz_bits(g) != 0;
+        const uint64_t bl = __builtin_amdgcn_ballot_w64(any);
+        if (bl != 0) {  // uniform
+          const int l0 = __builtin_ctzll(bl);
+          first = 4 * (64 * g + l0) + __builtin_ctz((unsigned)__builtin_amdgcn_readlane((int)nz_bits(g), l0));
         }
       }
       if (lane == 0 && first != 0x7fffffff) atomicMin(&found, (int)(wb + first));
@@ -123,25 +138,38 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
       else if (cb + kPlanChunk >= seq_len) doc_len = seq_len;  // no non-document slot at all
       if (doc_len < 0) continue;  // the whole chunk is document (uniform)
     }
-    // 2. visible slots past the prefix, ranked in slot order: r in [lo, hi)
+    // 2. visible slots past the prefix, ranked in slot order: r in [lo, hi).
+    // A stream sees few of the slots past the prefix, so rows wholly outside
+    // [lo, hi) are skipped, a row inside costs one id test per slot and one
+    // ballot, and the per-slot visibility bits and ranks are worked out only
+    // on rows that hold a candidate (id 0 or s + 1).
     const int lo = (int)max<int64_t>(min<int64_t>(doc_len - wb, kPlanWaveSpan), 0);
     unsigned m[kPlanG];
     int row_base[kPlanG];
     int wave_total = 0;
+    unsigned rows_hit = 0;  // (uniform) rows of the wave that hold a visible slot
 #pragma unroll
     for (int g = 0; g < kPlanG; ++g) {
-      const int ids[4] = {x[g].x, x[g].y, x[g].z, x[g].w};
       m[g] = 0;
+      row_base[g] = wave_total;
+      if (!live || 256 * (g + 1) <= lo || 256 * g >= hi) continue;  // (uniform)
+      const int4 y = x[g];
+      const bool cand = (y.x == 0) | (y.x == s1) | (y.y == 0) | (y.y == s1) | (y.z == 0) | (y.z == s1) |
+                        (y.w == 0) | (y.w == s1);
+      if (__builtin_amdgcn_ballot_w64(cand) == 0) continue;  // (uniform)
+      const int ids[4] = {y.x, y.y, y.z, y.w};
+      unsigned mg = 0;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * (64 * g + lane) + e;
-        const unsigned vis = (unsigned)(r >= lo) & (unsigned)(r < hi) & live &
-                             ((unsigned)(ids[e] == 0) | (unsigned)(ids[e] == s1));
-        m[g] |= vis << e;
+        mg |= ((unsigned)(r >= lo) & (unsigned)(r < hi) & ((unsigned)(ids[e] == 0) | (unsigned)(ids[e] == s1)))
+              << e;
       }
-      row_base[g] = wave_total;
+      m[g] = mg;
+      if (__builtin_amdgcn_ballot_w64(mg != 0) == 0) continue;  // (uniform) its candidates lie outside [lo, hi)
+      rows_hit |= 1u << g;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) wave_total += __popcll(__builtin_amdgcn_ballot_w64((m[g] >> e) & 1u));
+      for (int e = 0; e < 4; ++e) wave_total += __popcll(__builtin_amdgcn_ballot_w64((mg >> e) & 1u));
     }
     if (lane == 0) wsum[wave] = wave_total;
     __syncthreads();
@@ -155,6 +183,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     if (wave_total > 0) {  // uniform
 #pragma unroll
       for (int g = 0; g < kPlanG; ++g) {
+        if (!((rows_hit >> g) & 1u)) continue;  // (uniform)
         // matches of this row in earlier lanes (all four bits), then own bits
         int rank = row_base[g];
 #pragma unroll
