@@ -181,6 +181,24 @@ def test_plan_headline_shape_canonical_and_permuted():
     _plan_check(pc.stream_id.numpy(), pc.seq_len, pc.P, cap=2048)
 
 
+@pytest.mark.parametrize("doc", [0, 1, 255, 256, 257, 2047, 2048, 2049, 32767, 32768, 32769])
+def test_plan_prefix_and_end_at_row_and_wave_edges(doc):
+    # the plan reads ids in rows of 256 slots, 2048 per wave and 32768 per
+    # round, and skips rows outside [doc_len, seq_len): the prefix end and the
+    # sequence end on and around those edges, with late document slots and
+    # foreign ids in the tail
+    rng = np.random.default_rng(doc + 17)
+    P = 5
+    n = 4100
+    ids = np.concatenate([np.zeros(doc), rng.integers(1, P + 1, n)]).astype(np.int32)
+    ids[doc + rng.integers(1, n, 6)] = 0
+    ids[doc + rng.integers(1, n, 6)] = P + 3
+    T = len(ids)
+    for seq_len in sorted({T, doc + 1, doc + 255, doc + 256, doc + 257, doc + 2048, doc + 2049, T - 1}):
+        if 1 <= seq_len <= T:
+            _plan_check(ids, seq_len, P)
+
+
 @pytest.mark.parametrize("P", [1, 1023, 1024, 1025])
 def test_plan_stream_counts_around_the_two_pass_limit(P):
     # up to 1024 streams the plan takes two passes over chunks of the ids, past that one pass per stream

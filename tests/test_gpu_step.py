@@ -73,6 +73,33 @@ def test_step_plan_writes_ids_and_the_plan(shape):
         np.testing.assert_array_equal(sl[s, :n], lists[s][:n])
 
 
+@pytest.mark.parametrize("T0", [255, 256, 2047, 2048, 2049, 32767, 32768])
+def test_step_plan_new_slots_at_row_and_wave_edges(T0):
+    # the step's new slots start on and around the edges of the plan kernel's
+    # rows (256 slots), waves (2048) and rounds (32768), behind stale ids
+    rng = np.random.default_rng(T0)
+    P = 300
+    ids0 = np.zeros(T0, dtype=np.int32)
+    ids0[T0 // 2:] = rng.integers(1, P + 1, T0 - T0 // 2)
+    cap_total = T0 + P + 300
+    ids = np.concatenate([ids0, rng.integers(0, P + 5, cap_total - T0).astype(np.int32)])
+    sid = _i32(ids)
+    say(f"  gpu: pp_step_plan T0={T0} P={P}")
+    head, counts, slots = pp.pp_step_plan(sid, _i32([T0]), P, max_seq_len=cap_total, tail_capacity=2048)
+    torch.cuda.synchronize()
+    want = ids.copy()
+    want[T0:T0 + P] = np.arange(1, P + 1)
+    np.testing.assert_array_equal(sid.cpu().numpy(), want)
+    d_ref, lists = tail_lists(want, T0 + P, P)
+    assert head.cpu().tolist() == [d_ref, T0 + P]
+    c = counts.cpu().numpy()
+    sl = slots.cpu().numpy()
+    for s in range(P):
+        assert c[s] == len(lists[s]), s
+        n = min(len(lists[s]), 2048)
+        np.testing.assert_array_equal(sl[s, :n], lists[s][:n])
+
+
 @pytest.mark.parametrize("base", [-1, 60])
 def test_step_plan_out_of_range_base_is_an_empty_step(base):
     P, T = 8, 64
