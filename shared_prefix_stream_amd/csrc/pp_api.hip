@@ -191,6 +191,9 @@ pp_status_t decode_impl(Path path, const void* q, const void* k, const void* v, 
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   const float c = (float)((double)scale * 1.4426950408889634074);  // log2(e): softmax in base 2
   const int n_splits = path == Path::kParallel ? pl.doc.n_splits : pl.batched_splits;
+  // the keys and values a step may read (K and V up to the bound seq_len):
+  // past the last-level cache they are streamed with the non-temporal hint
+  const bool stream_nt = 2.0 * (double)nkv > pp::kLastLevelCacheBytes;
   pp::Workspace ws = pp::carve_workspace(workspace, n_splits, (int64_t)B * P, H, d, seq_len, B);
   if (xp) {  // the caller's plan (read only) in place of the plan kernel's
     ws.plan = const_cast<int32_t*>(xp->doc_len);
@@ -222,13 +225,13 @@ pp_status_t decode_impl(Path path, const void* q, const void* k, const void* v, 
   if (e == hipSuccess) {
     stage(1);
     e = path == Path::kParallel
-            ? pp::launch_doc(pl.doc, q, k, v, seq_len, P, Hkv, d, dtype, c, ws, stream, false, bt)
+            ? pp::launch_doc(pl.doc, q, k, v, seq_len, P, Hkv, d, dtype, c, ws, stream, false, bt, nullptr, stream_nt)
             : pp::launch_batched_doc(n_splits, q, k, v, seq_len, P, H, d, dtype, c, ws, stream, bt);
     unstage();
   }
   if (e == hipSuccess) {
     stage(2);
-    e = pp::launch_tail_merge(n_splits, q, k, v, sid, seq_len, P, H, d, dtype, c, ws, out, stream, bt);
+    e = pp::launch_tail_merge(n_splits, q, k, v, sid, seq_len, P, H, d, dtype, c, ws, out, stream, bt, stream_nt);
     unstage();
   }
   if (e != hipSuccess) return fail(PP_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));

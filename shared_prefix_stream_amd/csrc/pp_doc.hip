@@ -44,21 +44,39 @@ constexpr int kDocThreads = 256;  // workgroup of the fp32 vector-ALU kernel
 // The LDS base (and below the global base) is wave-uniform; readfirstlane
 // states it, since a call inside a branch on the wave's group may not be
 // known uniform to the compiler.
+// NT: the rows are read by this workgroup only, once per step, so they go
+// through the caches with the non-temporal hint and do not evict what the
+// step reads again (the split partials, the queries, the slot lists, the
+// own-slot rows) or force write-backs of dirty lines.
+template <bool NT>
 __device__ __forceinline__ void lds_dma16(const void* gaddr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(__builtin_amdgcn_readfirstlane(lds_base)),
-               "v"(gaddr)
-               : "memory", "m0");
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(
+                     __builtin_amdgcn_readfirstlane(lds_base)),
+                 "v"(gaddr)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(__builtin_amdgcn_readfirstlane(lds_base)),
+                 "v"(gaddr)
+                 : "memory", "m0");
 }
 // The same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane
 // byte offset (no 64-bit address arithmetic on the vector ALUs).
+template <bool NT>
 __device__ __forceinline__ void lds_dma16_sv(const void* base, uint32_t voff, uint32_t lds_base) {
   const uint64_t b = (uint64_t)base;
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
   const void* sbase = (const void*)(((uint64_t)hi << 32) | (uint64_t)lo);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(__builtin_amdgcn_readfirstlane(lds_base)),
-               "v"(voff), "s"(sbase)
-               : "memory", "m0");
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(
+                     __builtin_amdgcn_readfirstlane(lds_base)),
+                 "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(__builtin_amdgcn_readfirstlane(lds_base)),
+                 "v"(voff), "s"(sbase)
+                 : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
@@ -152,7 +170,10 @@ __device__ __forceinline__ void wait_vmcnt() {
 // longest first.  A document slot's whole visible set lies in its tile's
 // range, so with `out` given its output is final here and written directly
 // (the per-slot kernel that follows skips those slots).
-template <int D, int QB, int NW, bool CAUSAL>
+//
+// NT (non-causal, one query tile per key/value head): no other workgroup
+// reads this workgroup's key/value tiles, so they are loaded non-temporal.
+template <int D, int QB, int NW, bool CAUSAL, bool NT = false>
 __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int P,
     int H, float c, const int32_t* __restrict__ plan, int64_t seq_len, int n_splits,
@@ -286,8 +307,8 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
           const int blk = i * NW + wave_u + 4 * sset;
-          lds_dma16_sv(kt, koff[sset][i], ks + blk * 1024);
-          lds_dma16_sv(vt, voff[sset][i], vs + blk * 1024);
+          lds_dma16_sv<NT>(kt, koff[sset][i], ks + blk * 1024);
+          lds_dma16_sv<NT>(vt, voff[sset][i], vs + blk * 1024);
         }
     } else {
       asm volatile("" ::: "memory");  // (the ragged tile: a real branch)
@@ -299,8 +320,8 @@ __global__ __launch_bounds__(64 * NW) void doc_mfma_bf16_kernel(
           const int r = blk * TL::ROWS_PER_KB + lane / CPR;
           const int slot = lane % CPR;
           const int64_t g = (int64_t)min(kbase + r, key_end - 1) * row + (int64_t)hk * D;
-          lds_dma16(k + g + (slot ^ swz_k<D>(r)) * 8, ks + blk * 1024);
-          lds_dma16(v + g + (slot ^ swz_v<D>(r)) * 8, vs + blk * 1024);
+          lds_dma16<NT>(k + g + (slot ^ swz_k<D>(r)) * 8, ks + blk * 1024);
+          lds_dma16<NT>(v + g + (slot ^ swz_v<D>(r)) * 8, vs + blk * 1024);
         }
     }
   };
@@ -749,17 +770,22 @@ int doc_query_tile(const DocPlan& pl, pp_dtype_t dtype) {
 
 hipError_t launch_doc(const DocPlan& pl, const void* q, const void* k, const void* v, int64_t seq_len, int P, int H,
                       int d, pp_dtype_t dtype, float c, const Workspace& ws, hipStream_t stream, bool causal,
-                      const Batch& bt, void* out) {
+                      const Batch& bt, void* out, bool stream_nt) {
   const dim3 grid(pl.n_splits, H, pl.n_ptiles * bt.B);
   if (dtype == PP_BF16) {
     auto* qq = static_cast<const uint16_t*>(q);
     auto* kk = static_cast<const uint16_t*>(k);
     auto* vv = static_cast<const uint16_t*>(v);
-#define PP_DOC_LAUNCH(DD, QQ, WW)                                                                           \
-  (causal ? launch_kernel(doc_mfma_bf16_kernel<DD, QQ, WW, true>, grid, dim3(64 * WW), stream, qq, kk, vv, P, H, \
-                          c, ws.plan, seq_len, pl.n_splits, ws.part_o, ws.part_ml, bt, static_cast<uint16_t*>(out)) \
-          : launch_kernel(doc_mfma_bf16_kernel<DD, QQ, WW, false>, grid, dim3(64 * WW), stream, qq, kk, vv, P,    \
-                          H, c, ws.plan, seq_len, pl.n_splits, ws.part_o, ws.part_ml, bt, nullptr))
+    // one query tile per key/value head: each tile of keys and values is read
+    // by one workgroup only
+    const bool nt = stream_nt && !causal && pl.n_ptiles == 1 && bt.kv_group == 1;
+#define PP_DOC_LAUNCH(DD, QQ, WW)                                                                                 \
+  (causal ? launch_kernel(doc_mfma_bf16_kernel<DD, QQ, WW, true>, grid, dim3(64 * WW), stream, qq, kk, vv, P, H,       \
+                          c, ws.plan, seq_len, pl.n_splits, ws.part_o, ws.part_ml, bt, static_cast<uint16_t*>(out))       \
+   : nt   ? launch_kernel(doc_mfma_bf16_kernel<DD, QQ, WW, false, true>, grid, dim3(64 * WW), stream, qq, kk, vv, P, \
+                          H, c, ws.plan, seq_len, pl.n_splits, ws.part_o, ws.part_ml, bt, nullptr)                        \
+          : launch_kernel(doc_mfma_bf16_kernel<DD, QQ, WW, false>, grid, dim3(64 * WW), stream, qq, kk, vv, P, H, c,     \
+                          ws.plan, seq_len, pl.n_splits, ws.part_o, ws.part_ml, bt, nullptr))
     // dispatch on the exact (d, 16-query blocks per wave, waves) triple
     const int cfg = d * 10000 + pl.qb * 100 + pl.nw;
     switch (cfg) {

@@ -392,6 +392,15 @@ hipError_t launch_append_rope(const void* q, const void* k_new, const void* v_ne
 // Document part, all P queries of a head at once: split-K partial softmax
 // states over [0, doc_len).  Returns the number of splits it will use via
 // choose_doc_splits (host side, shape only).
+// Last-level cache of the device (MI355X: 256 MB of Infinity Cache, shared
+// by its XCDs).  A decode step whose key/value reads exceed it cannot keep
+// them cached until the next step, so the rows each workgroup reads once
+// are loaded with the non-temporal hint: they then do not evict what the
+// step reads again (split partials, queries, slot lists) or force
+// write-backs of dirty lines.  Smaller steps load them normally and may find
+// them cached on the next call.
+constexpr double kLastLevelCacheBytes = 256.0 * 1024 * 1024;
+
 struct DocPlan {
   int n_splits;
   int qb;        // 16-query blocks per wave (bf16 MFMA path)
@@ -405,9 +414,11 @@ int doc_query_tile(const DocPlan& plan, pp_dtype_t dtype);
 // slots j < min((pt + 1) * tile, doc_len) with j <= i (one split); with out
 // given, the rows of document slots (complete there) are written to it.
 // (P: streams per request, H: key/value heads; the grid covers bt.B requests)
+// stream_nt: load key/value tiles that only one workgroup reads with the
+// non-temporal hint (see kLastLevelCacheBytes).
 hipError_t launch_doc(const DocPlan& plan, const void* q, const void* k, const void* v, int64_t seq_len, int P,
                       int H, int d, pp_dtype_t dtype, float scale_log2, const Workspace& ws, hipStream_t stream,
-                      bool causal = false, const Batch& bt = Batch(), void* out = nullptr);
+                      bool causal = false, const Batch& bt = Batch(), void* out = nullptr, bool stream_nt = false);
 
 // Per-question document part (the "batched requests" baseline): every
 // stream reads the document itself.
@@ -420,10 +431,12 @@ hipError_t launch_batched_doc(int n_splits, const void* q, const void* k, const 
 // Own-slot gather for every stream, then the fixed-order merge of the doc
 // partials and the stream's own partial; writes out.
 // (P: streams per request, H: query heads)
+// stream_nt: load the own-slot rows with the non-temporal hint where no
+// other workgroup reads them (no grouped heads).
 hipError_t launch_tail_merge(int n_splits, const void* q, const void* k, const void* v,
                              const int32_t* sid, int64_t seq_len, int P, int H, int d, pp_dtype_t dtype,
                              float scale_log2, const Workspace& ws, void* out, hipStream_t stream,
-                             const Batch& bt = Batch());
+                             const Batch& bt = Batch(), bool stream_nt = false);
 
 // Prefill: for every query slot i in [doc_len, seq_len), the visible slots
 // the document kernel (causal, query tile `tile`) left out -- j in

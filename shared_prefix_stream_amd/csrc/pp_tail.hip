@@ -89,7 +89,11 @@ __device__ __forceinline__ void merge_state(float& M, float& Ls, float* A, float
 // j in [min((i / tile + 1) * tile, doc_len), i] with id 0 or id[i] -- what
 // the causal document kernel did not cover of i's visible set.  Slots below
 // doc_len are complete in the document kernel, which wrote them.
-template <typename T, int D, bool PREFILL>
+//
+// NT (decode without grouped heads): a stream's rows are read by its own
+// workgroups only, each its own slice, once per step: they are loaded
+// non-temporal, so that they do not evict what the step reads again.
+template <typename T, int D, bool PREFILL, bool NT = false>
 // (at most 128 VGPRs: four workgroups per CU)
 __global__ __launch_bounds__(kTailThreads, 4) void tail_merge_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ sid,
@@ -195,8 +199,13 @@ __global__ __launch_bounds__(kTailThreads, 4) void tail_merge_kernel(
 #pragma unroll
         for (int i = 0; i < kTailNI; ++i) {
           const int64_t off = (int64_t)j * row + (int64_t)(safe_head[i] / bt.G) * D + d0[i];
-          kr[u][i] = *reinterpret_cast<const u32x4*>(k + off);
-          vr[u][i] = *reinterpret_cast<const u32x4*>(v + off);
+          if constexpr (NT) {
+            kr[u][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k + off));
+            vr[u][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v + off));
+          } else {
+            kr[u][i] = *reinterpret_cast<const u32x4*>(k + off);
+            vr[u][i] = *reinterpret_cast<const u32x4*>(v + off);
+          }
         }
       }
 #pragma unroll
@@ -295,24 +304,31 @@ __global__ __launch_bounds__(kTailThreads, 4) void tail_merge_kernel(
 template <typename T, int D, bool PREFILL = false>
 hipError_t launch_tail_t(int n_splits, const void* q, const void* k, const void* v, const int32_t* sid,
                          int64_t seq_len, int P, int H, float c, const Workspace& ws, void* out, hipStream_t stream,
-                         int tile = 0, const Batch& bt = Batch()) {
+                         int tile = 0, const Batch& bt = Batch(), bool stream_nt = false) {
   using S = TailShape<T, D>;
   const dim3 grid(P * bt.B, (H + S::GW - 1) / S::GW);
-  return launch_kernel(tail_merge_kernel<T, D, PREFILL>, grid, dim3(kTailThreads), stream, static_cast<const T*>(q),
-                       static_cast<const T*>(k), static_cast<const T*>(v), sid, seq_len, P, H, c, ws.plan, ws.counts,
-                       ws.slots, ws.cap, n_splits, ws.part_o, ws.part_ml, static_cast<T*>(out), ws.dyn_len, tile, bt);
+  auto go = [&](auto kern) {
+    return launch_kernel(kern, grid, dim3(kTailThreads), stream, static_cast<const T*>(q), static_cast<const T*>(k),
+                         static_cast<const T*>(v), sid, seq_len, P, H, c, ws.plan, ws.counts, ws.slots, ws.cap,
+                         n_splits, ws.part_o, ws.part_ml, static_cast<T*>(out), ws.dyn_len, tile, bt);
+  };
+  // (grouped heads: the query heads of a key/value head read the same rows)
+  if constexpr (!PREFILL)
+    if (stream_nt && bt.G == 1) return go(tail_merge_kernel<T, D, false, true>);
+  return go(tail_merge_kernel<T, D, PREFILL>);
 }
 
 }  // namespace
 
 hipError_t launch_tail_merge(int n_splits, const void* q, const void* k, const void* v, const int32_t* sid,
                              int64_t seq_len, int P, int H, int d, pp_dtype_t dtype, float c, const Workspace& ws,
-                             void* out, hipStream_t stream, const Batch& bt) {
+                             void* out, hipStream_t stream, const Batch& bt, bool stream_nt) {
+  const bool nt = stream_nt;
   if (dtype == PP_BF16)
-    return d == 128 ? launch_tail_t<uint16_t, 128>(n_splits, q, k, v, sid, seq_len, P, H, c, ws, out, stream, 0, bt)
-                    : launch_tail_t<uint16_t, 64>(n_splits, q, k, v, sid, seq_len, P, H, c, ws, out, stream, 0, bt);
-  return d == 128 ? launch_tail_t<float, 128>(n_splits, q, k, v, sid, seq_len, P, H, c, ws, out, stream, 0, bt)
-                  : launch_tail_t<float, 64>(n_splits, q, k, v, sid, seq_len, P, H, c, ws, out, stream, 0, bt);
+    return d == 128 ? launch_tail_t<uint16_t, 128>(n_splits, q, k, v, sid, seq_len, P, H, c, ws, out, stream, 0, bt, nt)
+                    : launch_tail_t<uint16_t, 64>(n_splits, q, k, v, sid, seq_len, P, H, c, ws, out, stream, 0, bt, nt);
+  return d == 128 ? launch_tail_t<float, 128>(n_splits, q, k, v, sid, seq_len, P, H, c, ws, out, stream, 0, bt, nt)
+                  : launch_tail_t<float, 64>(n_splits, q, k, v, sid, seq_len, P, H, c, ws, out, stream, 0, bt, nt);
 }
 
 hipError_t launch_prefill_rest(int n_splits, int tile, const void* q, const void* k, const void* v,
