@@ -16,6 +16,9 @@ sys.path.insert(0, ROOT)
 import bench  # noqa: E402
 
 WORKLOAD = "codellama7b_doc16k_p256"
+# the headline's document kernel (d = 128, 2 query blocks, 8 waves, decode,
+# non-temporal key/value loads)
+DOC_KERNEL = "doc_mfma_bf16_kernel<128, 2, 8, false, true>"
 
 
 def _kv(path):
@@ -78,7 +81,7 @@ def test_kernel_trace_summary_gives_the_roofline(monkeypatch):
     avg = bench.read_trace_avg_us("document", WORKLOAD)
     assert avg is not None and 20.0 < avg < 500.0
     # the row the reader picked is the document kernel's
-    row = next(ln for ln in open(path) if ln.startswith("doc_mfma_bf16_kernel<128, 2, 8, false>"))
+    row = next(ln for ln in open(path) if ln.startswith(DOC_KERNEL))
     assert float(row.split(">", 1)[1].split()[1]) == avg
     # frac = algorithmic bytes / average duration / 8 TB/s
     frac = 270_532_608 / (avg * 1e-6) / 1e9 / 8000.0
@@ -159,11 +162,11 @@ def test_headline_trace_and_counters_agree_on_the_kernel_time():
     # the counter run's cycles over the trace's average give a plausible
     # shader clock (the two runs measure the same kernel)
     sq = open(os.path.join(ROOT, "profiles", f"pmc_sq_{WORKLOAD}.txt")).read()
-    m = re.search(r"document \(doc_mfma_bf16_kernel<128, 2, 8, false>\): dispatches \d+, kernel-trace avg ([\d.]+) us", sq)
+    m = re.search(r"document \(" + re.escape(DOC_KERNEL) + r"\): dispatches \d+, kernel-trace avg ([\d.]+) us", sq)
     assert m
     avg_sq = float(m.group(1))
     kt = open(os.path.join(ROOT, "profiles", f"kernels_{WORKLOAD}.txt")).read()
-    row = next(ln for ln in kt.splitlines() if ln.startswith("doc_mfma_bf16_kernel<128, 2, 8, false>"))
+    row = next(ln for ln in kt.splitlines() if ln.startswith(DOC_KERNEL))
     assert abs(float(row.split(">", 1)[1].split()[1]) - avg_sq) < 0.05 * avg_sq
     g = re.search(r"document \(doc_mfma.*?GRBM_GUI_ACTIVE\s+(\d+)", sq, re.S)
     ghz = int(g.group(1)) / 8.0 / (avg_sq * 1e3)
