@@ -29,34 +29,31 @@ namespace {
 
 constexpr int kAppendThreads = 256;
 
+// 16 bytes of elements <-> floats (8 bf16 or 4 fp32)
 template <typename T>
-__device__ __forceinline__ void load4(const T* p, float* f);
+__device__ __forceinline__ void unpack16(const u32x4& w, float* f);
 template <>
-__device__ __forceinline__ void load4<uint16_t>(const uint16_t* p, float* f) {
-  const uint2 w = *reinterpret_cast<const uint2*>(p);
-  f[0] = bf16_bits_to_f32(w.x & 0xffffu);
-  f[1] = bf16_bits_to_f32(w.x >> 16);
-  f[2] = bf16_bits_to_f32(w.y & 0xffffu);
-  f[3] = bf16_bits_to_f32(w.y >> 16);
+__device__ __forceinline__ void unpack16<uint16_t>(const u32x4& w, float* f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
+    f[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+  }
 }
 template <>
-__device__ __forceinline__ void load4<float>(const float* p, float* f) {
-  const float4 w = *reinterpret_cast<const float4*>(p);
-  f[0] = w.x;
-  f[1] = w.y;
-  f[2] = w.z;
-  f[3] = w.w;
+__device__ __forceinline__ void unpack16<float>(const u32x4& w, float* f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(w[i]);
 }
-
 template <typename T>
-__device__ __forceinline__ void store4(T* p, const float* f);
+__device__ __forceinline__ u32x4 pack16(const float* f);
 template <>
-__device__ __forceinline__ void store4<uint16_t>(uint16_t* p, const float* f) {
-  *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
+__device__ __forceinline__ u32x4 pack16<uint16_t>(const float* f) {
+  return u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
 }
 template <>
-__device__ __forceinline__ void store4<float>(float* p, const float* f) {
-  *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
+__device__ __forceinline__ u32x4 pack16<float>(const float* f) {
+  return u32x4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3])};
 }
 
 // Workgroup (s, b): stream s of request b.  plan = {doc_len[B], seq_len[B]}
@@ -68,6 +65,12 @@ __device__ __forceinline__ void store4<float>(float* p, const float* f) {
 // b - 1's.  A retired stream (active[s] == 0) lists nothing, so it has no
 // position: its query is rotated (the attention discards it) but its key and
 // value are not written.
+//
+// A rotation item is VE consecutive pairs (i, i + d/2) of one row: two
+// 16-byte vectors.  Each thread loads its first kPre items and value
+// vectors before anything else, so that one memory round trip (overlapping
+// the angles) precedes the rotation; rows past that (many heads) are
+// loaded in the loop.
 template <typename T, int D>
 __global__ __launch_bounds__(kAppendThreads) void append_rope_kernel(
     const T* __restrict__ q, const T* __restrict__ k_new, const T* __restrict__ v_new, T* __restrict__ k_cache,
@@ -75,8 +78,9 @@ __global__ __launch_bounds__(kAppendThreads) void append_rope_kernel(
     const int32_t* __restrict__ counts, int64_t max_len, T* __restrict__ q_rot, int64_t kv_stride,
     const int32_t* __restrict__ active) {
   constexpr int HALF = D / 2;
-  constexpr int C4 = HALF / 4;                 // items of 4 pairs per row
-  constexpr int VE = 16 / (int)sizeof(T);      // elements per 16-byte vector
+  constexpr int VE = 16 / (int)sizeof(T);  // elements per 16-byte vector
+  constexpr int CV = HALF / VE;            // rotation items per row
+  constexpr int kPre = 4;                  // items (and value vectors) per thread loaded up front
   __shared__ float cs[HALF], sn[HALF];
   const int s = blockIdx.x, P = gridDim.x, b = blockIdx.y, B = gridDim.y, tid = threadIdx.x;
   const int sl = b * P + s;  // stream of the launch
@@ -84,23 +88,25 @@ __global__ __launch_bounds__(kAppendThreads) void append_rope_kernel(
   v_cache += b * kv_stride;
   // rotation items: the Hq query rows of the stream, then its Hkv key rows
   const bool live = !active || active[sl] != 0;
-  const int nq = Hq * C4, nr = live ? (Hq + Hkv) * C4 : nq, nv = live ? Hkv * D / VE : 0;
+  const int nq = Hq * CV, nr = live ? (Hq + Hkv) * CV : nq, nv = live ? Hkv * D / VE : 0;
   const int64_t qoff = (int64_t)sl * Hq * D, knoff = (int64_t)sl * Hkv * D;
   auto row_off = [&](int it) -> int64_t {  // offset of item it within its rows
     const int r = it < nq ? it : it - nq;
-    return (int64_t)(r / C4) * D + (r % C4) * 4;
+    return (int64_t)(r / CV) * D + (r % CV) * VE;
   };
   auto src = [&](int it) -> const T* { return (it < nq ? q + qoff : k_new + knoff) + row_off(it); };
-  // Only the destination slot and the angle depend on the plan: the first
-  // item's inputs are loaded together with it, so one memory round trip
-  // precedes the rotation instead of three.
-  float a[4], b4[4];
-  u32x4 vv = {0, 0, 0, 0};
-  if (tid < nr) {
-    load4<T>(src(tid), a);
-    load4<T>(src(tid) + HALF, b4);
+  // Only the destination slot and the angle depend on the plan: every input
+  // this thread needs first is loaded before it.
+  u32x4 av[kPre], bv[kPre], vv[kPre];
+#pragma unroll
+  for (int p = 0; p < kPre; ++p) {
+    const int it = tid + p * kAppendThreads, iv = it;
+    if (it < nr) {
+      av[p] = *reinterpret_cast<const u32x4*>(src(it));
+      bv[p] = *reinterpret_cast<const u32x4*>(src(it) + HALF);
+    }
+    if (iv < nv) vv[p] = *reinterpret_cast<const u32x4*>(v_new + knoff + (int64_t)iv * VE);
   }
-  if (tid < nv) vv = *reinterpret_cast<const u32x4*>(v_new + knoff + (int64_t)tid * VE);
   const int32_t doc_len = plan[b], count = counts[sl];
   const int64_t seq_len = __builtin_amdgcn_readfirstlane(plan[B + b]);
   if (seq_len < P || seq_len > max_len) return;  // (uniform over the workgroup)
@@ -120,15 +126,14 @@ __global__ __launch_bounds__(kAppendThreads) void append_rope_kernel(
     }
     __syncthreads();
   }
-  for (int it = tid; it < nr; it += kAppendThreads) {
-    if (it != tid) {
-      load4<T>(src(it), a);
-      load4<T>(src(it) + HALF, b4);
-    }
-    const int i0 = (it % C4) * 4;
+  auto rotate_store = [&](int it, const u32x4& aw, const u32x4& bw) {
+    float a[VE], b4[VE];
+    unpack16<T>(aw, a);
+    unpack16<T>(bw, b4);
     if (rot) {
+      const int i0 = (it % CV) * VE;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
+      for (int e = 0; e < VE; ++e) {
         const float c = cs[i0 + e], sv = sn[i0 + e];
         const float x = a[e], y = b4[e];
         a[e] = fmaf(x, c, -y * sv);
@@ -136,13 +141,24 @@ __global__ __launch_bounds__(kAppendThreads) void append_rope_kernel(
       }
     }
     T* dst = (it < nq ? q_rot + qoff : k_cache + koff) + row_off(it);
-    store4<T>(dst, a);
-    store4<T>(dst + HALF, b4);
+    *reinterpret_cast<u32x4*>(dst) = pack16<T>(a);
+    *reinterpret_cast<u32x4*>(dst + HALF) = pack16<T>(b4);
+  };
+#pragma unroll
+  for (int p = 0; p < kPre; ++p) {
+    const int it = tid + p * kAppendThreads;
+    if (it < nr) rotate_store(it, av[p], bv[p]);
   }
-  for (int it = tid; it < nv; it += kAppendThreads) {
-    if (it != tid) vv = *reinterpret_cast<const u32x4*>(v_new + knoff + (int64_t)it * VE);
-    *reinterpret_cast<u32x4*>(v_cache + koff + (int64_t)it * VE) = vv;
+  for (int it = tid + kPre * kAppendThreads; it < nr; it += kAppendThreads)
+    rotate_store(it, *reinterpret_cast<const u32x4*>(src(it)), *reinterpret_cast<const u32x4*>(src(it) + HALF));
+#pragma unroll
+  for (int p = 0; p < kPre; ++p) {
+    const int iv = tid + p * kAppendThreads;
+    if (iv < nv) *reinterpret_cast<u32x4*>(v_cache + koff + (int64_t)iv * VE) = vv[p];
   }
+  for (int iv = tid + kPre * kAppendThreads; iv < nv; iv += kAppendThreads)
+    *reinterpret_cast<u32x4*>(v_cache + koff + (int64_t)iv * VE) =
+        *reinterpret_cast<const u32x4*>(v_new + knoff + (int64_t)iv * VE);
 }
 
 }  // namespace
