@@ -8,8 +8,10 @@ import numpy as np
 import pytest
 import torch
 
+import shared_prefix_stream_amd as pp
+from oracle import oracle_decode
 from tests.gpu_helpers import assert_close, reference, run
-from workloads import make_case
+from workloads import make_case, multi_case
 
 pytestmark = pytest.mark.gpu
 
@@ -37,3 +39,21 @@ def test_steps_past_the_last_level_cache(P, H, D, doc, dtype):
     assert 2 * case.seq_len * H * D * es > LLC_BYTES  # the non-temporal variants run
     streams = sorted({0, P - 1, *rng.choice(P, 4, replace=False).tolist()})
     assert_close(run(case, "decode"), reference(case, streams=streams), streams=streams, what=case.name)
+
+
+def test_two_requests_past_the_last_level_cache():
+    # several requests per launch (each its own caches, request strides in
+    # the kernels' addressing) with the non-temporal variants
+    case = multi_case(32, 32, 128, 60, [9000, 8000], q_range=(1, 40), a_len=7, seed=21, name="llc_two_requests")
+    B, T = case.k.shape[0], case.k.shape[1]
+    assert 2 * B * T * 32 * 128 * 2 > LLC_BYTES
+    q, k, v, sid = (t.to("cuda:0") for t in (case.q, case.k, case.v, case.stream_id))
+    lens = torch.tensor(case.seq_lens, dtype=torch.int32, device="cuda:0")
+    out = pp.pp_attn_decode_multi(q, k, v, sid, lens, scale=case.scale)
+    torch.cuda.synchronize()
+    streams = [0, 17, 38, 59]
+    for b in range(B):
+        n = case.seq_lens[b]
+        ref = oracle_decode(case.q[b], case.k[b, :n], case.v[b, :n], case.stream_id[b].numpy(), n, case.scale,
+                            streams=streams)
+        assert_close(out[b], ref, streams, what=f"{case.name} request {b}")
